@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked GQA attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workloads a,b] [--no-cpu-baseline]
+
+A step is one attention call (one pass of the whole path: band plan, K/V
+staging, Q.K^T, softcap, mask, online softmax, P.V, epilogue, and for decode
+the split partials and their fixed-order merge) over one batch of seeded
+synthetic input already resident in HBM.  The headline workload is the GQA
+4:1 decode over 8192 cached keys (B=8, Hq=32, Hkv=8, d=128), reported in
+GB/s of algorithmic bytes; the other workloads are measured the same way and
+listed under "workloads" (TFLOP/s for prefill/encoder, GB/s for decode).
+
+Timing: W untimed calls, then exactly K calls between two HIP events on the
+stream the kernels run on, bracketed by device synchronisation.  Inputs
+rotate over several copies so that repeated calls stream from HBM rather than
+from the 256 MB last-level cache.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "decode_gqa4_kv8192"
+METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 MFMA
+LLC_BYTES = 256 * 1024 * 1024    # MI355X last-level (Infinity) cache
+KERNEL_SRC = os.path.join(ROOT, "masked_gqa_attention_amd", "csrc", "mgqa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_decode_gqa4_kv8192.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+class Runner:
+    """Device copies of one workload and a lean C-ABI call per copy."""
+
+    def __init__(self, w, copies):
+        import torch
+        from masked_gqa_attention_amd import _lib, synth
+        self.torch = torch
+        self.w = w
+        q, k, v = synth.draw_qkv(w)
+        self.host = (q, k, v)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        np_int = "int16"
+
+        def dev(a):
+            if w.dtype == "bf16":
+                return torch.from_numpy(a.view(np_int)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(a).cuda()
+
+        base = [dev(a) for a in (q, k, v)]
+        self.sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+        self.outs = [torch.empty_like(base[0]) for _ in range(copies)]
+        self.ws_bytes = _lib.attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d,
+                                                  int(w.causal), w.window)
+        self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.fn = _lib.load().attn_fwd_ex
+        dtype_code = _lib.MGQA_BF16 if w.dtype == "bf16" else _lib.MGQA_FP16
+        self.args = []
+        for (tq, tk, tv), to in zip(self.sets, self.outs):
+            self.args.append((tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), to.data_ptr(),
+                              w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
+                              ctypes.c_float(w.softcap), dtype_code,
+                              self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes,
+                              self.stream))
+        del dt
+
+    def call(self, i):
+        rc = self.fn(*self.args[i % len(self.args)])
+        if rc != 0:
+            from masked_gqa_attention_amd import _lib
+            raise RuntimeError(f"attn_fwd_ex failed: {_lib.error_string(rc)}")
+
+    def time(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.call(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            self.call(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps  # ms per call
+
+    def output_f64(self, i=0):
+        from masked_gqa_attention_amd import synth
+        o = self.outs[i % len(self.outs)]
+        torch = self.torch
+        if self.w.dtype == "bf16":
+            arr = o.view(torch.int16).cpu().numpy().view("uint16")
+        else:
+            arr = o.cpu().numpy()
+        return synth.storage_to_f64(arr, self.w.dtype)
+
+
+def copies_for(w) -> int:
+    from masked_gqa_attention_amd import accounting
+    touched = accounting.workload_work(w)["bytes"]
+    return max(2, min(32, -(-2 * LLC_BYTES // max(touched, 1))))
+
+
+def figures(w, ms):
+    from masked_gqa_attention_amd import accounting
+    wk = accounting.workload_work(w)
+    decode = w.Lq * w.G <= 16
+    if decode:
+        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+        return {"unit": "GB/s", "value": gbs, "bound": "hbm", "peak": HBM_PEAK_GBS,
+                "frac": gbs / HBM_PEAK_GBS, "alg_bytes": wk["bytes"], "alg_flops": wk["flops"]}
+    tf = wk["flops"] / (ms * 1e-3) / 1e12
+    return {"unit": "TFLOP/s", "value": tf, "bound": "mfma", "peak": MFMA_PEAK_TFLOPS,
+            "frac": tf / MFMA_PEAK_TFLOPS, "alg_bytes": wk["bytes"], "alg_flops": wk["flops"]}
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(runner, gpu_out):
+    """The float64 oracle, as it stands, on the headline workload's input
+    (all rows), timed on this host; also the GPU output's error against it."""
+    import numpy as np
+    import oracle
+    from masked_gqa_attention_amd import accounting, synth
+    w = runner.w
+    q, k, v = runner.host
+    qf, kf, vf = (synth.storage_to_f64(a, w.dtype) for a in (q, k, v))
+    times = []
+    t_total = time.perf_counter()
+    ref = None
+    while len(times) < 5 and (time.perf_counter() - t_total) < 20.0:
+        t0 = time.perf_counter()
+        ref = oracle.attention(qf, kf, vf, w.causal, w.window, w.softcap)
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[len(times) // 2]
+    wk = accounting.workload_work(w)
+    err = np.abs(gpu_out - ref)
+    ok = bool(np.isfinite(gpu_out).all() and (err <= 2e-2 + 2e-2 * np.abs(ref)).all())
+    return {
+        "value": wk["bytes"] / t / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+        "sample": f"whole {w.name} input ({w.B * w.Hq * w.Lq} query rows x {w.Lkv} keys), "
+                  f"median of {len(times)} runs, {t:.3f} s each",
+        "seconds": t, "parity_vs_gpu": {"ok": ok, "max_abs_err": float(err.max())},
+    }
+
+
+def load_traffic(steps_kernel_ms):
+    """Counter-derived HBM bytes per launch of the headline kernel, if the
+    counters were taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workloads", default="all",
+                    help="comma list of extra workloads to measure besides the headline, or 'all'/'none'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (batch, kv head) unit is independent; see the sharding note in the design "
+              "document). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from masked_gqa_attention_amd import _lib, synth
+    _lib.load()
+
+    names = [HEADLINE]
+    if args.workloads == "all":
+        names += [n for n in synth.WORKLOAD_ORDER if n != HEADLINE]
+    elif args.workloads != "none":
+        names += [n for n in args.workloads.split(",") if n and n != HEADLINE]
+
+    results = {}
+    headline = None
+    for name in names:
+        w = synth.WORKLOADS[name]
+        copies = copies_for(w)
+        log(f"{name}: {copies} input copies")
+        r = Runner(w, copies)
+        if name == HEADLINE:
+            steps, warmup = args.steps, args.warmup
+        else:
+            r.call(0)
+            torch.cuda.synchronize()
+            est = r.time(3, 1)
+            steps = int(max(10, min(2000, 200.0 / max(est, 1e-3))))
+            warmup = max(3, steps // 10)
+        ms = r.time(steps, warmup)
+        fig = figures(w, ms)
+        rc, plan = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
+                                  w.softcap, 0 if w.dtype == "bf16" else 1)
+        results[name] = {"ms": ms, "steps": steps, "copies": copies, **fig,
+                         "kernel": "decode_kernel" if plan.get("path") == 1 else "prefill_kernel",
+                         "plan": plan, "shape": w.describe()}
+        log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
+            f"({100 * fig['frac']:.1f}% of {fig['bound']} peak)")
+        if name == HEADLINE:
+            headline = (r, ms, steps, fig)
+        else:
+            del r
+            torch.cuda.empty_cache()
+
+    r, ms, steps, fig = headline
+    w = r.w
+    gpu_out = r.output_f64((steps - 1) % len(r.outs))
+    traffic = load_traffic(ms)
+    line = {
+        "metric": METRIC,
+        "value": fig["value"],
+        "unit": fig["unit"],
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V (PCG64, Q then K then V), resident in HBM",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
+                   "Lkv": w.Lkv, "d": w.d, "causal": w.causal, "window": w.window,
+                   "softcap": w.softcap, "seed": w.seed, "input_copies": len(r.outs)},
+        "roofline": {"bound": "hbm", "achieved": fig["value"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": fig["frac"], "traffic": traffic,
+                     "kernel": results[HEADLINE]["kernel"],
+                     "alg_bytes_per_launch": fig["alg_bytes"]},
+        "workloads": {n: {k: v for k, v in res.items() if k not in ("shape",)}
+                      for n, res in results.items()},
+        "device": torch.cuda.get_device_name(0),
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(r, gpu_out)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

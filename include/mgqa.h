@@ -1,0 +1,116 @@
+/*
+ * mgqa.h - C ABI of the MI355X (gfx950) masked grouped-query attention library.
+ *
+ * Operation (task page "TPU v6e Masked GQA Kernel Optimization", sections
+ * "What You Have", "What You Submit" and "Hard Constraints"): the attention
+ * forward pass over decode, prefill and encoder shapes with GQA ratios 1:1 to
+ * 16:1, an optional causal mask, an optional sliding window and an optional
+ * logit softcap; output in the input precision and in Q's shape; same inputs
+ * give the same output bits.  For every batch b, query head h, query row i:
+ *
+ *   O[b,h,i,:] = sum_j softmax_j( mask( softcap( Q[b,h,i,:].K[b,g,j,:] / sqrt(d) ) ) ) V[b,g,j,:]
+ *
+ * with these readings of points the page leaves open:
+ *   - g = h / (Hq/Hkv): consecutive query heads share one K/V head;
+ *   - scale 1/sqrt(d), d the head size passed in (no padding involved);
+ *   - softcap c > 0: s -> c*tanh(s/c) on the scaled score, before the mask;
+ *   - causal mask aligned bottom-right: row i sits at key position
+ *     p = i + Lkv - Lq and sees keys j <= p;
+ *   - window W > 0: keys with p - j < W (W keys including the diagonal); without
+ *     the causal mask also j - p < W;
+ *   - a causal mask or a window with Lq > Lkv is rejected (rows would be empty).
+ *
+ * Layout: all tensors are dense row-major, element offsets computed in 64 bit:
+ *   q, out : [B][Hq ][Lq ][d]      k, v : [B][Hkv][Lkv][d]
+ * Element type: bf16 for attn_fwd; bf16 or fp16 for attn_fwd_ex (out has the
+ * input type).  Accumulation and softmax are fp32.  All tensor pointers are
+ * device pointers, 16-byte aligned; d must be a multiple of 8 (16-byte rows).
+ *
+ * Ownership: the caller owns q, k, v, out and any workspace.  The library keeps
+ * no pointer after a call returns; the buffers must stay valid until the work
+ * queued on `stream` has finished.  q, k, v are read only; out must not overlap
+ * them.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ * All work of one call is queued on that stream; calls return without waiting.
+ *
+ * Errors: every entry point returns 0 on success or a negative MGQA_ERR_* code.
+ * Arguments are validated before any HIP call; on a validation error nothing
+ * is queued.  Faults inside a kernel surface at the caller's next
+ * synchronisation, as usual for HIP.  attn_error_string() gives the text.
+ *
+ * Determinism: the kernel choice, tiling and split plan depend on the shape
+ * and options only, no float atomics are used and every reduction has a fixed
+ * order, so identical inputs give bit-identical outputs on one device and build.
+ */
+#ifndef MGQA_H
+#define MGQA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MGQA_OK             0
+#define MGQA_ERR_NULL      -1  /* a required pointer is NULL                         */
+#define MGQA_ERR_SHAPE     -2  /* a size <= 0, Hq % Hkv != 0 or Hq/Hkv > 16           */
+#define MGQA_ERR_HEAD_DIM  -3  /* d not a multiple of 8 or d > 128                    */
+#define MGQA_ERR_MASK      -4  /* window < 0, causal not 0/1, or mask with Lq > Lkv   */
+#define MGQA_ERR_SOFTCAP   -5  /* softcap negative, NaN or infinite                   */
+#define MGQA_ERR_ALIGN     -6  /* a tensor pointer not 16-byte aligned                */
+#define MGQA_ERR_WORKSPACE -7  /* workspace missing or smaller than required          */
+#define MGQA_ERR_HIP       -8  /* a HIP runtime call or kernel launch failed          */
+#define MGQA_ERR_DTYPE     -9  /* dtype not MGQA_BF16 / MGQA_FP16                      */
+#define MGQA_ERR_RANGE    -10  /* a size too large for the library's 32-bit indexing  */
+
+#define MGQA_BF16 0
+#define MGQA_FP16 1
+
+/* Masked GQA attention forward, bf16 in and out.  window <= 0 means no window,
+ * softcap <= 0 means no softcap, causal is 0 or 1.  Allocates its own
+ * stream-ordered workspace when the split decode path needs one
+ * (hipMallocAsync / hipFreeAsync on `stream`). */
+int attn_fwd(const void* q, const void* k, const void* v, void* out,
+             int B, int Hq, int Hkv, int Lq, int Lkv, int d,
+             int causal, int window, float softcap, void* stream);
+
+/* Bytes of workspace attn_fwd_ex needs for this shape (0 when the planned path
+ * needs none).  Returns 0 as well for arguments attn_fwd_ex would reject. */
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lkv, int d,
+                            int causal, int window);
+
+/* Same operation with an explicit element type (MGQA_BF16 or MGQA_FP16) and a
+ * caller-provided workspace of at least attn_workspace_bytes() bytes (may be
+ * NULL when that is 0).  The workspace holds fp32 split partials and per-unit
+ * arrival counters.  It must be zero-filled before its first use; every call
+ * that completes leaves the counters at zero again, so one workspace can be
+ * reused by later calls on the same stream without clearing.  Calls that run
+ * concurrently (different streams) must use different workspaces. */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                int B, int Hq, int Hkv, int Lq, int Lkv, int d,
+                int causal, int window, float softcap, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Plan the library would use for this shape, without touching the GPU.
+ * info[0] path (0 = prefill/encoder kernel, 1 = split-KV decode kernel)
+ * info[1] workgroups launched
+ * info[2] query rows (head, position pairs) per workgroup
+ * info[3] key splits per (batch, kv-head) unit (1 on the prefill path)
+ * info[4] keys per tile
+ * info[5] padded head size used for Q.K^T (multiple of 32)
+ * info[6] padded head size used for P.V (multiple of 16)
+ * info[7] workspace bytes
+ * Returns 0 or a validation error code (then info is untouched). */
+int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d,
+              int causal, int window, float softcap, int dtype, long long info[8]);
+
+/* Static text for an error code (never NULL). */
+const char* attn_error_string(int code);
+
+/* Library ABI version (major*100 + minor). */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGQA_H */

@@ -1,0 +1,104 @@
+"""ctypes binding of libmgqa.so: the C-ABI entry points of include/mgqa.h under
+the same names, argument marshalling only.
+
+torch is imported before the library is opened so that the HIP runtime torch
+already loaded (same SONAME) is the one the library binds to.  A missing
+library raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmgqa.so")
+
+# Error codes (include/mgqa.h)
+MGQA_OK = 0
+MGQA_ERR_NULL = -1
+MGQA_ERR_SHAPE = -2
+MGQA_ERR_HEAD_DIM = -3
+MGQA_ERR_MASK = -4
+MGQA_ERR_SOFTCAP = -5
+MGQA_ERR_ALIGN = -6
+MGQA_ERR_WORKSPACE = -7
+MGQA_ERR_HIP = -8
+MGQA_ERR_DTYPE = -9
+MGQA_ERR_RANGE = -10
+
+MGQA_BF16 = 0
+MGQA_FP16 = 1
+
+# Every symbol the header declares.
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_workspace_bytes", "attn_plan",
+           "attn_error_string", "attn_version")
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Open libmgqa.so (once) and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} not found: build it with `python -m masked_gqa_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_fwd_ex.restype = i
+    lib.attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_workspace_bytes.restype = sz
+    lib.attn_plan.argtypes = [i, i, i, i, i, i, i, i, f, i, ctypes.POINTER(ctypes.c_longlong)]
+    lib.attn_plan.restype = i
+    lib.attn_error_string.argtypes = [i]
+    lib.attn_error_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def error_string(code: int) -> str:
+    return load().attn_error_string(code).decode()
+
+
+def attn_fwd(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, stream) -> int:
+    return load().attn_fwd(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window),
+                           float(softcap), stream)
+
+
+def attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype,
+                workspace, workspace_bytes, stream) -> int:
+    return load().attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window),
+                              float(softcap), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def attn_workspace_bytes(B, Hq, Hkv, Lq, Lkv, d, causal, window) -> int:
+    return int(load().attn_workspace_bytes(B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window)))
+
+
+PLAN_FIELDS = ("path", "workgroups", "rows_per_wg", "nsplit", "keys_per_tile", "d_qk_pad",
+               "d_pv_pad", "workspace_bytes")
+
+
+def attn_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype=MGQA_BF16):
+    """Returns (code, dict) -- dict is empty when code != 0."""
+    info = (ctypes.c_longlong * 8)()
+    rc = load().attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window), float(softcap),
+                          int(dtype), info)
+    if rc != 0:
+        return rc, {}
+    return rc, dict(zip(PLAN_FIELDS, list(info)))
+
+
+def attn_version() -> int:
+    return int(load().attn_version())

@@ -1,0 +1,240 @@
+// C-ABI front end: argument validation, the shape-only plan, workspace
+// layout and the launch on the caller's stream.  See include/mgqa.h for the
+// contract of every entry point.
+#include "mgqa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "mgqa_internal.h"
+
+namespace mgqa {
+namespace {
+
+constexpr int kCUs = 256;              // MI355X compute units
+constexpr long long kTargetWGs = 512;  // decode: aim for two workgroups per CU
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int validate(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
+             float softcap, int dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lkv <= 0 || d <= 0) return MGQA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq / Hkv > 16) return MGQA_ERR_SHAPE;
+  if (d % 8 != 0 || d > 128) return MGQA_ERR_HEAD_DIM;
+  if (causal != 0 && causal != 1) return MGQA_ERR_MASK;
+  if (window < 0) return MGQA_ERR_MASK;
+  if ((causal || window > 0) && Lq > Lkv) return MGQA_ERR_MASK;
+  if (!(softcap >= 0.f) || isinf(softcap)) return MGQA_ERR_SOFTCAP;  // also rejects NaN
+  if (dtype != MGQA_BF16 && dtype != MGQA_FP16) return MGQA_ERR_DTYPE;
+  // 32-bit indexing inside the kernels: per-tensor element counts and grid size.
+  const long long q_elems = (long long)B * Hq * Lq * d;
+  const long long kv_elems = (long long)B * Hkv * Lkv * d;
+  if (q_elems > (1LL << 40) || kv_elems > (1LL << 40)) return MGQA_ERR_RANGE;
+  if ((long long)Lkv * d >= (1LL << 31) || (long long)Lq * Hq >= (1LL << 31)) return MGQA_ERR_RANGE;
+  return MGQA_OK;
+}
+
+}  // namespace
+
+int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
+              float softcap, int dtype, Plan* plan) {
+  const int err = validate(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype);
+  if (err) return err;
+  Plan p = {};
+  const int G = Hq / Hkv;
+  p.dqk = (d + 31) / 32;
+  p.dv = (d <= 80 && d > 64) ? 5 : 2 * p.dqk;  // 72 and 80 use a 80-wide P.V
+  const long long units = (long long)B * Hkv;
+
+  if (G * Lq <= kMaxRowsDecode) {
+    p.path = kPathDecode;
+    p.keys_per_tile = kDecodeKeys;
+    p.rows_per_wg = kMaxRowsDecode;
+    p.nqb = 1;
+    const int off = Lkv - Lq;
+    const int key_lo = window > 0 ? (off - window + 1 > 0 ? off - window + 1 : 0) : 0;
+    const int t_begin = key_lo / kDecodeKeys;
+    const int t_end = (Lkv - 1) / kDecodeKeys + 1;
+    const int tiles = t_end - t_begin;
+    long long ns = (kTargetWGs + units - 1) / units;
+    if (ns > tiles) ns = tiles;
+    if (ns < 1) ns = 1;
+    const int tps = (int)((tiles + ns - 1) / ns);
+    ns = (tiles + tps - 1) / tps;
+    p.nsplit = (int)ns;
+    p.tiles_per_split = tps;
+    p.workgroups = units * ns;
+    if (ns > 1) {
+      const size_t nrows = (size_t)G * Lq;
+      const size_t o_bytes = (size_t)units * ns * nrows * (p.dv * 16) * sizeof(float);
+      const size_t ml_bytes = (size_t)units * ns * nrows * 2 * sizeof(float);
+      const size_t cnt_bytes = (size_t)units * sizeof(unsigned);
+      p.ws_cnt_off = 0;
+      p.ws_ml_off = align_up(cnt_bytes, 256);
+      p.ws_o_off = align_up(p.ws_ml_off + ml_bytes, 256);
+      p.ws_bytes = align_up(p.ws_o_off + o_bytes, 256);
+    }
+  } else {
+    p.path = kPathPrefill;
+    p.keys_per_tile = kPrefillKeys;
+    p.nsplit = 1;
+    // Largest query block that still gives at least two workgroups per CU;
+    // the smallest block otherwise.
+    int nqb = 1;
+    for (int cand = 4; cand >= 1; cand /= 2) {
+      const int m = 64 * cand / G;
+      const long long wgs = units * ((Lq + m - 1) / m);
+      if (wgs >= 2 * kCUs) {
+        nqb = cand;
+        break;
+      }
+    }
+    p.nqb = nqb;
+    p.rows_per_wg = 64 * nqb;
+    const int m = p.rows_per_wg / G;
+    p.workgroups = units * ((Lq + m - 1) / m);
+  }
+  if (p.workgroups >= (1LL << 31)) return MGQA_ERR_RANGE;
+  *plan = p;
+  return MGQA_OK;
+}
+
+static KernelArgs make_args(const Plan& p, const void* q, const void* k, const void* v, void* out,
+                            int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
+                            float softcap, void* ws) {
+  KernelArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Lq = Lq;
+  a.Lkv = Lkv;
+  a.d = d;
+  a.causal = causal;
+  a.window = window;
+  const double log2e = 1.4426950408889634;
+  a.alpha = (float)(log2e / sqrt((double)d));
+  if (softcap > 0.f) {
+    a.gamma = (float)(2.0 * log2e / ((double)softcap * sqrt((double)d)));
+    a.c2 = (float)((double)softcap * log2e);
+    a.beta = (float)(1.0 / ((double)softcap * sqrt((double)d)));
+  }
+  if (p.path == kPathPrefill) {
+    a.m = p.rows_per_wg / a.G;
+    a.n_pos_blk = (Lq + a.m - 1) / a.m;
+    a.nsplit = 1;
+  } else {
+    const int off = Lkv - Lq;
+    const int key_lo = window > 0 ? (off - window + 1 > 0 ? off - window + 1 : 0) : 0;
+    a.t_begin = key_lo / kDecodeKeys;
+    a.t_end = (Lkv - 1) / kDecodeKeys + 1;
+    a.nsplit = p.nsplit;
+    a.tiles_per_split = p.tiles_per_split;
+    a.nrows = a.G * Lq;
+    if (ws) {
+      char* base = static_cast<char*>(ws);
+      a.ws_cnt = reinterpret_cast<unsigned*>(base + p.ws_cnt_off);
+      a.ws_ml = reinterpret_cast<float*>(base + p.ws_ml_off);
+      a.ws_o = reinterpret_cast<float*>(base + p.ws_o_off);
+    }
+  }
+  return a;
+}
+
+}  // namespace mgqa
+
+using namespace mgqa;
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+extern "C" {
+
+int attn_version(void) { return 100; }
+
+const char* attn_error_string(int code) {
+  switch (code) {
+    case MGQA_OK: return "success";
+    case MGQA_ERR_NULL: return "a required pointer is NULL";
+    case MGQA_ERR_SHAPE: return "bad shape: sizes must be > 0, Hq a multiple of Hkv, Hq/Hkv <= 16";
+    case MGQA_ERR_HEAD_DIM: return "unsupported head size: d must be a multiple of 8 and <= 128";
+    case MGQA_ERR_MASK:
+      return "bad mask: causal must be 0/1, window >= 0, and Lq <= Lkv when a causal mask or window is set";
+    case MGQA_ERR_SOFTCAP: return "bad softcap: must be finite and >= 0";
+    case MGQA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case MGQA_ERR_WORKSPACE: return "workspace missing or smaller than attn_workspace_bytes()";
+    case MGQA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case MGQA_ERR_DTYPE: return "dtype must be MGQA_BF16 (0) or MGQA_FP16 (1)";
+    case MGQA_ERR_RANGE: return "a size exceeds the library's indexing range";
+    default: return "unknown error code";
+  }
+}
+
+int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
+              float softcap, int dtype, long long info[8]) {
+  if (!info) return MGQA_ERR_NULL;
+  Plan p;
+  const int err = make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, &p);
+  if (err) return err;
+  info[0] = p.path;
+  info[1] = p.workgroups;
+  info[2] = p.rows_per_wg;
+  info[3] = p.nsplit;
+  info[4] = p.keys_per_tile;
+  info[5] = p.dqk * 32;
+  info[6] = p.dv * 16;
+  info[7] = (long long)p.ws_bytes;
+  return MGQA_OK;
+}
+
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal,
+                            int window) {
+  Plan p;
+  if (make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, 0.f, MGQA_BF16, &p)) return 0;
+  return p.ws_bytes;
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                int Lq, int Lkv, int d, int causal, int window, float softcap, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out) return MGQA_ERR_NULL;
+  Plan p;
+  const int err = make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, &p);
+  if (err) return err;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MGQA_ERR_ALIGN;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return MGQA_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MGQA_ERR_ALIGN;
+  const KernelArgs a = make_args(p, q, k, v, out, Hq, Hkv, Lq, Lkv, d, causal, window, softcap,
+                                 p.ws_bytes ? workspace : nullptr);
+  if (launch(p, a, dtype, softcap > 0.f, stream) != hipSuccess) return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+             int Lq, int Lkv, int d, int causal, int window, float softcap, void* stream) {
+  if (!q || !k || !v || !out) return MGQA_ERR_NULL;
+  Plan p;
+  const int err = make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, MGQA_BF16, &p);
+  if (err) return err;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MGQA_ERR_ALIGN;
+  if (p.ws_bytes == 0)
+    return attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, MGQA_BF16,
+                       nullptr, 0, stream);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, p.ws_bytes, st) != hipSuccess) return MGQA_ERR_HIP;
+  // Only the counters must start at zero; the partials are always written first.
+  int rc = MGQA_OK;
+  if (launch_zero(ws, p.ws_ml_off / 4, stream) != hipSuccess) rc = MGQA_ERR_HIP;
+  if (rc == MGQA_OK)
+    rc = attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, MGQA_BF16, ws,
+                     p.ws_bytes, stream);
+  if (hipFreeAsync(ws, st) != hipSuccess && rc == MGQA_OK) rc = MGQA_ERR_HIP;
+  return rc;
+}
+
+}  // extern "C"

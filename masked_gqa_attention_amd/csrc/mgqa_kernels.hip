@@ -1,0 +1,625 @@
+// gfx950 (MI355X, CDNA4) kernels for masked grouped-query attention.
+//
+// Operation: the attention forward pass of the task page "TPU v6e Masked GQA
+// Kernel Optimization" ("What You Have": decode, prefill and encoder shapes,
+// GQA 1:1 to 16:1, optional causal mask, sliding window and logit softcap).
+// The score/probability products run on bf16/fp16 MFMA with fp32 accumulation
+// (the Graphcore page, "SigLIP batch-1 hardware results", uses the same split of
+// 16-bit products and 32-bit accumulation); the softmax is fp32 and streams
+// over key tiles (the "bounded-block" streaming form named on that page's
+// introduction), so the score matrix is never materialised.
+//
+// Layout of the work:
+//   * A workgroup owns one (batch, kv head) pair and a block of query rows.  A
+//     row is a (query head of the group, query position) pair, so one K/V tile
+//     staged in LDS feeds all G query heads that share the kv head.
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32:
+//     the accumulator layout of S^T (lane = query column, 4 consecutive key
+//     rows per lane group) is exactly the B-operand layout P^T needs for the
+//     second product O^T = V^T P^T, so probabilities never leave registers.
+//     The key order inside a 32-key step is permuted so each lane group holds
+//     8 consecutive keys, which makes the V^T operand one 16-byte LDS read.
+//   * K is staged row-major, V is staged transposed (V^T) in LDS; rows are
+//     padded by 16 bytes.
+//   * Tiles wholly outside the causal/window band are never visited; tiles
+//     wholly inside skip the mask arithmetic.
+//   * Online softmax in base 2 with a lazily updated reference maximum: the
+//     accumulators are rescaled only when a row maximum grows by more than
+//     2^8, so probabilities stay below 256 and most tiles skip the rescale.
+//   * Decode (G*Lq <= 16 rows per kv head) splits the key band over
+//     workgroups; each writes fp32 partials (max, sum, unnormalised output) and
+//     the last workgroup to arrive for a (batch, kv head) combines all splits in
+//     split order.  No float atomics: the result is bit-reproducible.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mgqa_internal.h"
+
+namespace mgqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+// Lazy rescale threshold in base-2 exponent units.
+constexpr float kRescaleSlack = 8.0f;
+
+// ---------------------------------------------------------------------------
+// Element-type traits: the MFMA and the float -> storage conversion.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<__bf16> {
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 h = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+template <>
+struct Elem<_Float16> {
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    f16x2 h = __builtin_convertvector(f, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Visibility of global key `j` to a row at absolute key position `pos`.
+__device__ __forceinline__ bool key_visible(int j, int pos, int Lkv, int causal, int window) {
+  bool ok = j < Lkv;
+  if (causal) ok = ok && (j <= pos);
+  if (window > 0) {
+    ok = ok && (pos - j < window);
+    if (!causal) ok = ok && (j - pos < window);
+  }
+  return ok;
+}
+
+// Maximum raw score -> base-2 exponent units (monotone map).
+template <bool SOFTCAP>
+__device__ __forceinline__ float max_to_exp_units(float mx, const KernelArgs& a) {
+  if (mx == kNegInf) return kNegInf;
+  if (SOFTCAP) return a.c2 * tanhf(mx * a.beta);
+  return mx * a.alpha;
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging.  K: [keys][DQK*32 + 8] row-major.  V^T: [DV*16][keys + 8].
+// Keys past Lkv and head-size columns past d are zero-filled, so padded
+// columns contribute exactly 0 to both products.
+// ---------------------------------------------------------------------------
+template <int KEYS, int DQK>
+__device__ __forceinline__ void stage_k(uint16_t* Ks, const uint16_t* kg, int k0, int Lkv, int d,
+                                        int tid) {
+  constexpr int KP = DQK * 32 + 8;
+  constexpr int CH = DQK * 4;  // 8-element chunks per padded row
+  constexpr int TOTAL = KEYS * CH;
+#pragma unroll
+  for (int c = tid; c < TOTAL; c += kThreads) {
+    const int key = c / CH, ch = c % CH;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (k0 + key < Lkv && ch * 8 < d) val = ldg16(kg + (size_t)(k0 + key) * d + ch * 8);
+    *reinterpret_cast<u32x4*>(Ks + key * KP + ch * 8) = val;
+  }
+}
+
+template <int KEYS, int DV>
+__device__ __forceinline__ void stage_vt(uint16_t* Vt, const uint16_t* vg, int k0, int Lkv, int d,
+                                         int tid) {
+  constexpr int VP = KEYS + 8;
+  constexpr int KG = KEYS / 4;    // 4-key groups
+  constexpr int DC = DV * 2;      // 8-column chunks of the padded head size
+  constexpr int TOTAL = KG * DC;
+#pragma unroll
+  for (int c = tid; c < TOTAL; c += kThreads) {
+    const int kgi = c % KG, dc = c / KG;
+    u16x8 rows[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + kgi * 4 + r;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (key < Lkv && dc * 8 < d) val = ldg16(vg + (size_t)key * d + dc * 8);
+      rows[r] = __builtin_bit_cast(u16x8, val);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u16x4 col = {rows[0][i], rows[1][i], rows[2][i], rows[3][i]};
+      *reinterpret_cast<u16x4*>(Vt + (dc * 8 + i) * VP + kgi * 4) = col;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One wave, NQB query blocks of 16 rows, NK32 steps of 32 keys starting at
+// tile-local key `kbase`.  Updates the online-softmax state in place.
+//
+// S^T block (step tt, half hh) row rho holds tile-local key
+//   kbase + 32*tt + 8*(rho/4) + 4*hh + rho%4,
+// so after the MFMA lane group g4 holds keys kbase + 32*tt + 8*g4 + [0..7]
+// across the two halves: the P^T operand of step tt, in key order.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, int NQB, int NK32, int KEYS, bool SOFTCAP>
+__device__ __forceinline__ void wave_step(const uint16_t* Ks, const uint16_t* Vt, int kbase,
+                                          int kglob0, bool full, const u32x4 (&qf)[NQB][DQK],
+                                          const int (&qpos)[NQB], float (&m_e)[NQB],
+                                          float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                          const KernelArgs& a, int lane) {
+  constexpr int KP = DQK * 32 + 8;
+  constexpr int VP = KEYS + 8;
+  const int c16 = lane & 15, g4 = lane >> 4;
+
+  // ---- S^T = K Q^T -------------------------------------------------------
+  f32x4 s[NQB][NK32][2];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) s[qb][tt][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int tt = 0; tt < NK32; ++tt) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int krow = kbase + 32 * tt + 8 * (c16 >> 2) + 4 * hh + (c16 & 3);
+#pragma unroll
+      for (int t = 0; t < DQK; ++t) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + krow * KP + 32 * t + 8 * g4);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][tt][hh] = Elem<T>::mfma(kf, qf[qb][t], s[qb][tt][hh]);
+      }
+    }
+  }
+
+  // ---- mask, online softmax, probabilities ---------------------------------
+  u32x4 pk[NQB][NK32];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (!full) {
+#pragma unroll
+      for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = kglob0 + kbase + 32 * tt + 8 * g4 + 4 * hh + i;
+            if (!key_visible(j, qpos[qb], a.Lkv, a.causal, a.window)) s[qb][tt][hh][i] = kNegInf;
+          }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][tt][hh][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxe = max_to_exp_units<SOFTCAP>(mx, a);
+    if (mxe > m_e[qb] + kRescaleSlack) {
+      const float f = fast_exp2(m_e[qb] - mxe);  // 0 when m_e was -inf
+      m_e[qb] = mxe;
+      l_p[qb] *= f;
+#pragma unroll
+      for (int db = 0; db < DV; ++db) o[qb][db] *= f;
+    }
+    const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
+    float lsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NK32; ++tt) {
+      float p[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = s[qb][tt][hh][i];
+          float pv;
+          if (SOFTCAP) {
+            // c*tanh(u) = c - 2c/(exp(2u)+1); in base-2 units the exponent is
+            // c2 - 2*c2*r - mref with r = 1/(2^(x*gamma) + 1).
+            const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
+            pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
+            if (!full && x == kNegInf) pv = 0.f;
+          } else {
+            pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
+          }
+          p[hh * 4 + i] = pv;
+          lsum += pv;
+        }
+      pk[qb][tt] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
+                         Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
+    }
+    l_p[qb] += lsum;
+  }
+
+  // ---- O^T += V^T P^T ----------------------------------------------------------
+#pragma unroll
+  for (int tt = 0; tt < NK32; ++tt) {
+#pragma unroll
+    for (int db = 0; db < DV; ++db) {
+      const u32x4 vf =
+          *reinterpret_cast<const u32x4*>(Vt + (db * 16 + c16) * VP + kbase + 32 * tt + 8 * g4);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[qb][tt], o[qb][db]);
+    }
+  }
+}
+
+// Load this lane's Q^T operand (16 query columns, 8 head-size elements per
+// lane group and 32-wide step).  Rows outside the problem load zeros.
+template <int DQK>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[DQK], const uint16_t* qrow, bool ok, int d,
+                                       int g4) {
+#pragma unroll
+  for (int t = 0; t < DQK; ++t) {
+    const int col = 32 * t + 8 * g4;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (ok && col < d) val = ldg16(qrow + col);
+    qf[t] = val;
+  }
+}
+
+// Store one lane's 16-row x (DV*16) output slice: lane column c16 is the row,
+// lane group g4 holds head-size columns 16*db + 4*g4 + [0..3].
+template <typename T, int DV>
+__device__ __forceinline__ void store_row(uint16_t* orow, const f32x4 (&o)[DV], float inv, int d,
+                                          int g4) {
+#pragma unroll
+  for (int db = 0; db < DV; ++db) {
+    const int col = 16 * db + 4 * g4;
+    if (col < d) {
+      u32x2 w = {Elem<T>::pack2(o[db][0] * inv, o[db][1] * inv),
+                 Elem<T>::pack2(o[db][2] * inv, o[db][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + col) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / encoder kernel: one workgroup per (batch, kv head, block of m
+// query positions); 4 waves x NQB x 16 rows; rows are (head of the group,
+// position) pairs with the head index fastest.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, int NQB, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(KernelArgs a) {
+  constexpr int KEYS = kPrefillKeys;
+  constexpr int KP = DQK * 32 + 8;
+  constexpr int VP = KEYS + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KEYS * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * 16 * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+
+  const int bid = blockIdx.x;
+  const int pblk = bid % a.n_pos_blk;
+  const int unit = bid / a.n_pos_blk;  // b * Hkv + kvh
+  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int G = a.G, d = a.d;
+  const int q0 = pblk * a.m;
+  const int m_eff = min(a.m, a.Lq - q0);
+  const int off = a.Lkv - a.Lq;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * d;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * d;
+  uint16_t* og = static_cast<uint16_t*>(a.out);
+
+  u32x4 qf[NQB][DQK];
+  int qpos[NQB];
+  bool rok[NQB];
+  size_t roff[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int r = (wave * NQB + qb) * 16 + c16;
+    const int pl = r / G, hr = r % G;
+    rok[qb] = pl < m_eff;
+    const int pos = q0 + pl;
+    qpos[qb] = pos + off;
+    const int head = kvh * G + hr;
+    roff[qb] = (((size_t)b * a.Hq + head) * a.Lq + (rok[qb] ? pos : 0)) * d;
+    load_q<DQK>(qf[qb], qg + roff[qb], rok[qb], d, g4);
+  }
+
+  // Key band of this block of positions.
+  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
+  int key_lo = 0, key_hi = a.Lkv - 1;
+  if (a.causal) key_hi = min(key_hi, pos_max);
+  if (a.window > 0) {
+    key_lo = max(0, pos_min - a.window + 1);
+    if (!a.causal) key_hi = min(key_hi, pos_max + a.window - 1);
+  }
+  const int t_begin = key_lo / KEYS, t_end = key_hi / KEYS + 1;
+
+  float m_e[NQB], l_p[NQB];
+  f32x4 o[NQB][DV];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_e[qb] = kNegInf;
+    l_p[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int k0 = t * KEYS;
+    __syncthreads();
+    stage_k<KEYS, DQK>(Ks, kg, k0, a.Lkv, d, tid);
+    stage_vt<KEYS, DV>(Vt, vg, k0, a.Lkv, d, tid);
+    __syncthreads();
+    bool full = k0 + KEYS <= a.Lkv;
+    if (a.causal) full = full && (k0 + KEYS - 1 <= pos_min);
+    if (a.window > 0) {
+      full = full && (pos_max - k0 < a.window);
+      if (!a.causal) full = full && (k0 + KEYS - 1 - pos_min < a.window);
+    }
+    wave_step<T, DQK, DV, NQB, KEYS / 32, KEYS, SOFTCAP>(Ks, Vt, 0, k0, full, qf, qpos, m_e, l_p,
+                                                          o, a, lane);
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float l = l_p[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, d, g4);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV decode kernel: one workgroup per (unit = batch*Hkv + kv head,
+// split).  The 16 rows are (head of the group, position) pairs, head fastest,
+// nrows = G*Lq <= 16 of them real.  Each 128-key tile is staged once; wave w
+// takes keys [32w, 32w+32).  The four wave states are merged in LDS, then the
+// split's partial is written, and the last split to arrive for the unit merges
+// all partials in split order and writes the output.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
+  constexpr int KEYS = kDecodeKeys;
+  constexpr int KP = DQK * 32 + 8;
+  constexpr int VP = KEYS + 8;
+  constexpr int DVP = DV * 16;
+  constexpr int OP = DVP + 4;  // LDS pitch of the merged wave outputs (floats)
+  // K and V^T tiles; after the key loop the same bytes hold the wave outputs.
+  constexpr int TILE_BYTES = (KEYS * KP + DVP * VP) * 2;
+  constexpr int MERGE_BYTES = 4 * 16 * OP * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vt = Ks + KEYS * KP;
+  float (*wo)[16 * OP] = reinterpret_cast<float (*)[16 * OP]>(smem);
+  __shared__ float wm[4][16], wl[4][16];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x % a.nsplit;
+  const int unit = blockIdx.x / a.nsplit;
+  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int G = a.G, d = a.d;
+  const int off = a.Lkv - a.Lq;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * d;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * d;
+  uint16_t* og = static_cast<uint16_t*>(a.out);
+
+  // This lane's row (column c16 of the single query block).
+  const int r = c16;
+  const bool rok = r < a.nrows;
+  const int pl = r / G, hr = r % G;
+  const int head = kvh * G + hr;
+  const size_t roff = (((size_t)b * a.Hq + head) * a.Lq + (rok ? pl : 0)) * d;
+  u32x4 qf[1][DQK];
+  int qpos[1] = {pl + off};
+  load_q<DQK>(qf[0], qg + roff, rok, d, g4);
+
+  float m_e[1] = {kNegInf}, l_p[1] = {0.f};
+  f32x4 o[1][DV];
+#pragma unroll
+  for (int db = 0; db < DV; ++db) o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int pos_min = off, pos_max = off + a.Lq - 1;
+  const int t0 = a.t_begin + split * a.tiles_per_split;
+  const int t1 = min(a.t_end, t0 + a.tiles_per_split);
+  for (int t = t0; t < t1; ++t) {
+    const int k0 = t * KEYS;
+    __syncthreads();
+    stage_k<KEYS, DQK>(Ks, kg, k0, a.Lkv, d, tid);
+    stage_vt<KEYS, DV>(Vt, vg, k0, a.Lkv, d, tid);
+    __syncthreads();
+    // Full-tile test on this wave's 32 keys.
+    const int w0 = k0 + 32 * wave;
+    bool full = w0 + 32 <= a.Lkv;
+    if (a.causal) full = full && (w0 + 31 <= pos_min);
+    if (a.window > 0) {
+      full = full && (pos_max - w0 < a.window);
+      if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
+    }
+    wave_step<T, DQK, DV, 1, 1, KEYS, SOFTCAP>(Ks, Vt, 32 * wave, k0, full, qf, qpos, m_e, l_p, o,
+                                               a, lane);
+  }
+
+  // ---- merge the four wave states (fixed order) -----------------------------
+  __syncthreads();  // every wave is done reading the tiles that wo overwrites
+  float l = l_p[0];
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (g4 == 0) {
+    wm[wave][c16] = m_e[0];
+    wl[wave][c16] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < DV; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wo[wave][c16 * OP + 16 * db + 4 * g4 + i] = o[0][db][i];
+  __syncthreads();
+
+  // Thread -> (row rr, 8-column chunk cc); 16 rows x DV*2 chunks <= 256.
+  const int rr = tid / (DV * 2), cc = tid % (DV * 2);
+  const bool active = (tid < 16 * DV * 2) && (rr < a.nrows);
+  float M = kNegInf, L = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (active) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][rr]);
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2(wm[w][rr] - M);
+        L += f * wl[w][rr];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += f * wo[w][rr * OP + cc * 8 + i];
+      }
+    }
+  }
+
+  if (a.nsplit == 1) {
+    if (active && cc * 8 < d) {
+      const float inv = 1.0f / L;
+      const size_t oo = (((size_t)b * a.Hq + kvh * G + rr % G) * a.Lq + rr / G) * d + cc * 8;
+      u32x4 w = {Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv),
+                 Elem<T>::pack2(acc[4] * inv, acc[5] * inv), Elem<T>::pack2(acc[6] * inv, acc[7] * inv)};
+      *reinterpret_cast<u32x4*>(og + oo) = w;
+    }
+    return;
+  }
+
+  // ---- write this split's partial ----------------------------------------------
+  const size_t pidx = ((size_t)unit * a.nsplit + split) * a.nrows;
+  if (active) {
+    float* po = a.ws_o + (pidx + rr) * DVP + cc * 8;
+    *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    if (cc == 0) {
+      a.ws_ml[(pidx + rr) * 2 + 0] = M;
+      a.ws_ml[(pidx + rr) * 2 + 1] = L;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(a.ws_cnt + unit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (prev == (unsigned)(a.nsplit - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+
+  // ---- last arrival: merge all splits in split order -------------------------------
+  if (active) {
+    const size_t base = (size_t)unit * a.nsplit * a.nrows;
+    float Mg = kNegInf;
+    for (int s = 0; s < a.nsplit; ++s)
+      Mg = fmaxf(Mg, __builtin_nontemporal_load(a.ws_ml + (base + (size_t)s * a.nrows + rr) * 2));
+    float Lg = 0.f, og8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) og8[i] = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+      const size_t pr = base + (size_t)s * a.nrows + rr;
+      const float ms = __builtin_nontemporal_load(a.ws_ml + pr * 2);
+      if (ms == kNegInf) continue;
+      const float f = fast_exp2(ms - Mg);
+      Lg += f * __builtin_nontemporal_load(a.ws_ml + pr * 2 + 1);
+      const float* po = a.ws_o + pr * DVP + cc * 8;
+      const f32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po));
+      const f32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        og8[i] += f * x0[i];
+        og8[4 + i] += f * x1[i];
+      }
+    }
+    if (cc * 8 < d) {
+      const float inv = 1.0f / Lg;
+      const size_t oo = (((size_t)b * a.Hq + kvh * G + rr % G) * a.Lq + rr / G) * d + cc * 8;
+      u32x4 w = {Elem<T>::pack2(og8[0] * inv, og8[1] * inv), Elem<T>::pack2(og8[2] * inv, og8[3] * inv),
+                 Elem<T>::pack2(og8[4] * inv, og8[5] * inv), Elem<T>::pack2(og8[6] * inv, og8[7] * inv)};
+      *reinterpret_cast<u32x4*>(og + oo) = w;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(a.ws_cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void zero_kernel(uint32_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch over the instantiated shapes.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, bool SOFTCAP>
+static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStream_t st) {
+  const dim3 block(kThreads);
+  const dim3 grid((unsigned)plan.workgroups);
+  if (plan.path == kPathDecode) {
+    hipLaunchKernelGGL((decode_kernel<T, DQK, DV, SOFTCAP>), grid, block, 0, st, args);
+  } else if (plan.nqb == 4) {
+    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 4, SOFTCAP>), grid, block, 0, st, args);
+  } else if (plan.nqb == 2) {
+    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, SOFTCAP>), grid, block, 0, st, args);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 1, SOFTCAP>), grid, block, 0, st, args);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, bool SOFTCAP>
+static hipError_t launch_dims(const Plan& plan, const KernelArgs& args, hipStream_t st) {
+  switch (plan.dqk * 16 + plan.dv) {
+    case 1 * 16 + 2: return launch_typed<T, 1, 2, SOFTCAP>(plan, args, st);
+    case 2 * 16 + 4: return launch_typed<T, 2, 4, SOFTCAP>(plan, args, st);
+    case 3 * 16 + 5: return launch_typed<T, 3, 5, SOFTCAP>(plan, args, st);
+    case 3 * 16 + 6: return launch_typed<T, 3, 6, SOFTCAP>(plan, args, st);
+    case 4 * 16 + 8: return launch_typed<T, 4, 8, SOFTCAP>(plan, args, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int launch(const Plan& plan, const KernelArgs& args, int dtype, bool softcap, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == 0)
+    return softcap ? launch_dims<__bf16, true>(plan, args, st) : launch_dims<__bf16, false>(plan, args, st);
+  return softcap ? launch_dims<_Float16, true>(plan, args, st) : launch_dims<_Float16, false>(plan, args, st);
+}
+
+int launch_zero(void* p, size_t words, void* stream) {
+  if (words == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((words + 255) / 256);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+}  // namespace mgqa

@@ -1,0 +1,140 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, rejects bad arguments before any HIP call, and plans the expected
+path for each workload.  No compute call is made here (no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from masked_gqa_attention_amd import _lib
+from masked_gqa_attention_amd.synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mgqa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libmgqa.so not built (python -m masked_gqa_attention_amd.build)")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_matches_binding_list():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_header_symbol():
+    lib = _lib.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+
+
+def test_version_and_error_strings():
+    assert _lib.attn_version() == 100
+    for code in range(-10, 1):
+        s = _lib.error_string(code)
+        assert s and s != "unknown error code"
+    assert _lib.error_string(-99) == "unknown error code"
+
+
+# Fake, 16-byte aligned, never dereferenced: every call below must fail
+# validation before anything reaches the GPU.
+P = ctypes.c_void_p(0x100000)
+MIS = ctypes.c_void_p(0x100008)
+
+
+def _ex(**kw):
+    a = dict(q=P, k=P, v=P, out=P, B=1, Hq=4, Hkv=1, Lq=64, Lkv=64, d=128, causal=1, window=0,
+             softcap=0.0, dtype=0, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.attn_fwd_ex(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"], a["Lq"],
+                            a["Lkv"], a["d"], a["causal"], a["window"], a["softcap"], a["dtype"],
+                            a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.MGQA_ERR_NULL),
+    (dict(out=None), _lib.MGQA_ERR_NULL),
+    (dict(B=0), _lib.MGQA_ERR_SHAPE),
+    (dict(Lq=-1), _lib.MGQA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), _lib.MGQA_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), _lib.MGQA_ERR_SHAPE),      # G = 17 > 16
+    (dict(d=100), _lib.MGQA_ERR_HEAD_DIM),
+    (dict(d=136), _lib.MGQA_ERR_HEAD_DIM),
+    (dict(causal=2), _lib.MGQA_ERR_MASK),
+    (dict(window=-1), _lib.MGQA_ERR_MASK),
+    (dict(Lq=65, Lkv=64), _lib.MGQA_ERR_MASK),       # causal with Lq > Lkv
+    (dict(Lq=65, Lkv=64, causal=0, window=8), _lib.MGQA_ERR_MASK),
+    (dict(softcap=-1.0), _lib.MGQA_ERR_SOFTCAP),
+    (dict(softcap=float("nan")), _lib.MGQA_ERR_SOFTCAP),
+    (dict(softcap=float("inf")), _lib.MGQA_ERR_SOFTCAP),
+    (dict(dtype=2), _lib.MGQA_ERR_DTYPE),
+    (dict(q=MIS), _lib.MGQA_ERR_ALIGN),
+    (dict(v=MIS), _lib.MGQA_ERR_ALIGN),
+    # decode shape that needs a workspace, none given
+    (dict(Hq=32, Hkv=8, Lq=1, Lkv=8192, B=8), _lib.MGQA_ERR_WORKSPACE),
+    (dict(Hq=32, Hkv=8, Lq=1, Lkv=8192, B=8, ws=P, wsb=16), _lib.MGQA_ERR_WORKSPACE),
+    (dict(Hq=32, Hkv=8, Lq=1, Lkv=8192, B=8, ws=ctypes.c_void_p(0x100010), wsb=1 << 30),
+     _lib.MGQA_ERR_ALIGN),
+])
+def test_validation_codes(kw, code):
+    assert _ex(**kw) == code
+
+
+def test_attn_fwd_validation_codes():
+    assert _lib.attn_fwd(None, P, P, P, 1, 4, 1, 64, 64, 128, 1, 0, 0.0, None) == _lib.MGQA_ERR_NULL
+    assert _lib.attn_fwd(P, P, P, P, 1, 4, 1, 64, 64, 100, 1, 0, 0.0, None) == _lib.MGQA_ERR_HEAD_DIM
+    assert _lib.attn_fwd(P, P, P, MIS, 1, 4, 1, 64, 64, 128, 1, 0, 0.0, None) == _lib.MGQA_ERR_ALIGN
+
+
+def test_non_causal_longer_query_is_allowed_in_plan():
+    # No mask and no window: every key is visible to every row, Lq > Lkv is fine.
+    rc, info = _lib.attn_plan(1, 2, 1, 100, 10, 64, 0, 0, 0.0)
+    assert rc == 0 and info["path"] == 0
+
+
+def test_plans_for_workloads():
+    paths = {}
+    for name, w in WORKLOADS.items():
+        rc, info = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
+                                  w.softcap, 1 if w.dtype == "fp16" else 0)
+        assert rc == 0, name
+        paths[name] = info
+        assert info["workgroups"] >= 1
+        assert info["d_qk_pad"] >= w.d and info["d_pv_pad"] >= w.d
+        ws = _lib.attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window)
+        assert ws == info["workspace_bytes"]
+    assert paths["decode_gqa4_kv8192"]["path"] == 1
+    assert paths["decode_gqa4_kv8192"]["nsplit"] > 1
+    assert paths["decode_gqa16_kv32768_w4096_cap30"]["path"] == 1
+    assert paths["prefill_gqa8_L4096_w1024_cap50"]["path"] == 0
+    assert paths["encoder_siglip_L729_d72"]["d_pv_pad"] == 80
+    assert paths["encoder_siglip_L729_d72"]["d_qk_pad"] == 96
+    # The decode band of the windowed decode covers only the last 4096 keys:
+    # its splits times keys per split must not exceed the window plus a tile.
+    info = paths["decode_gqa16_kv32768_w4096_cap30"]
+    w = WORKLOADS["decode_gqa16_kv32768_w4096_cap30"]
+    assert info["workgroups"] == w.B * w.Hkv * info["nsplit"]
+
+
+def test_workspace_layout_fits():
+    # The workspace size covers partials for every split, row and padded column.
+    for (B, Hq, Hkv, Lq, Lkv, d) in [(8, 32, 8, 1, 8192, 128), (4, 64, 4, 1, 32768, 128),
+                                     (3, 12, 4, 4, 5000, 72), (1, 16, 1, 1, 129, 64)]:
+        rc, info = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, 1, 0, 0.0)
+        assert rc == 0
+        if info["nsplit"] > 1:
+            G = Hq // Hkv
+            need = B * Hkv * info["nsplit"] * G * Lq * (info["d_pv_pad"] + 2) * 4 + B * Hkv * 4
+            assert info["workspace_bytes"] >= need
+        else:
+            assert info["workspace_bytes"] == 0
