@@ -14,7 +14,11 @@ namespace mgqa {
 namespace {
 
 constexpr int kCUs = 256;              // MI355X compute units
-constexpr long long kTargetWGs = 512;  // decode: aim for two workgroups per CU
+#ifndef MGQA_DECODE_TARGET_WGS
+#define MGQA_DECODE_TARGET_WGS 512
+#endif
+// Decode: split the key band until about this many workgroups run (two per CU).
+constexpr long long kTargetWGs = MGQA_DECODE_TARGET_WGS;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -92,6 +92,39 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Split partials cross workgroups (and XCDs, each with its own L2) through
+// device-scope stores and loads, which write through to and read from the
+// device coherence point.  The writer waits for its stores to
+// complete before it bumps the arrival counter, so the last arrival reads
+// complete partials.  This avoids device-scope fences, which on this chip
+// write back and invalidate the whole L2 of the XCD.
+// Buffer instructions carry the scope bits: kDeviceScope sets SC1 (device
+// scope, SC0 clear).  The descriptor's third dword is the gfx9 raw-buffer
+// format word (32-bit data format, no swizzle).
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_dev16(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void st_dev8(__amdgpu_buffer_rsrc_t rs, int off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4 ld_dev16(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kDeviceScope));
+}
+__device__ __forceinline__ f32x2 ld_dev8(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kDeviceScope));
+}
+// Wait until every vector-memory operation this wave issued has completed
+// (s_waitcnt vmcnt(0); the expcnt and lgkmcnt fields are left at "no wait").
+__device__ __forceinline__ void wait_vmem_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Visibility of global key `j` to a row at absolute key position `pos`.
 __device__ __forceinline__ bool key_visible(int j, int pos, int Lkv, int causal, int window) {
   bool ok = j < Lkv;
@@ -116,46 +149,90 @@ __device__ __forceinline__ float max_to_exp_units(float mx, const KernelArgs& a)
 // Keys past Lkv and head-size columns past d are zero-filled, so padded
 // columns contribute exactly 0 to both products.
 // ---------------------------------------------------------------------------
+//
+// A tile is moved in two phases so that every global load of a tile is in
+// flight at once and the next tile's loads overlap the current tile's math:
+// load() issues unconditional 16-byte loads into registers (an out-of-range
+// element reads the unit's first row instead and is then replaced by zero),
+// store() writes the registers to LDS.
 template <int KEYS, int DQK>
-__device__ __forceinline__ void stage_k(uint16_t* Ks, const uint16_t* kg, int k0, int Lkv, int d,
-                                        int tid) {
-  constexpr int KP = DQK * 32 + 8;
-  constexpr int CH = DQK * 4;  // 8-element chunks per padded row
-  constexpr int TOTAL = KEYS * CH;
-#pragma unroll
-  for (int c = tid; c < TOTAL; c += kThreads) {
-    const int key = c / CH, ch = c % CH;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (k0 + key < Lkv && ch * 8 < d) val = ldg16(kg + (size_t)(k0 + key) * d + ch * 8);
-    *reinterpret_cast<u32x4*>(Ks + key * KP + ch * 8) = val;
-  }
-}
+struct KTile {
+  static constexpr int KP = DQK * 32 + 8;
+  static constexpr int CH = DQK * 4;  // 8-element chunks per padded row
+  static constexpr int TOTAL = KEYS * CH;
+  static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
+  u32x4 r[PER];
+  uint32_t okmask;  // bit it: element `it` is inside the tensor (zero-filled otherwise)
 
-template <int KEYS, int DV>
-__device__ __forceinline__ void stage_vt(uint16_t* Vt, const uint16_t* vg, int k0, int Lkv, int d,
-                                         int tid) {
-  constexpr int VP = KEYS + 8;
-  constexpr int KG = KEYS / 4;    // 4-key groups
-  constexpr int DC = DV * 2;      // 8-column chunks of the padded head size
-  constexpr int TOTAL = KG * DC;
+  __device__ __forceinline__ void load(const uint16_t* kg, int k0, int Lkv, int d, int tid) {
+    okmask = 0u;
 #pragma unroll
-  for (int c = tid; c < TOTAL; c += kThreads) {
-    const int kgi = c % KG, dc = c / KG;
-    u16x8 rows[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + kgi * 4 + r;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (key < Lkv && dc * 8 < d) val = ldg16(vg + (size_t)key * d + dc * 8);
-      rows[r] = __builtin_bit_cast(u16x8, val);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u16x4 col = {rows[0][i], rows[1][i], rows[2][i], rows[3][i]};
-      *reinterpret_cast<u16x4*>(Vt + (dc * 8 + i) * VP + kgi * 4) = col;
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * kThreads;
+      const int key = c / CH, ch = c % CH;
+      const bool ok = (TOTAL % kThreads == 0 || c < TOTAL) && (k0 + key < Lkv) && (ch * 8 < d);
+      r[it] = ldg16(ok ? kg + (size_t)(k0 + key) * d + ch * 8 : kg);
+      okmask |= ok ? (1u << it) : 0u;
     }
   }
-}
+  __device__ __forceinline__ void store(uint16_t* Ks, int tid) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * kThreads;
+      if (TOTAL % kThreads == 0 || c < TOTAL)
+        *reinterpret_cast<u32x4*>(Ks + (c / CH) * KP + (c % CH) * 8) =
+            ((okmask >> it) & 1u) ? r[it] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+};
+
+// Each thread moves 4 consecutive keys x 8 head-size columns and writes them
+// transposed: 8 LDS rows of V^T, 4 keys (8 bytes) each.
+template <int KEYS, int DV>
+struct VtTile {
+  static constexpr int VP = KEYS + 8;
+  static constexpr int KG = KEYS / 4;  // 4-key groups
+  static constexpr int DC = DV * 2;    // 8-column chunks of the padded head size
+  static constexpr int TOTAL = KG * DC;
+  static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
+  u32x4 r[PER][4];
+  uint32_t okmask;  // bit 4*it + rr: element inside the tensor (zero-filled otherwise)
+
+  __device__ __forceinline__ void load(const uint16_t* vg, int k0, int Lkv, int d, int tid) {
+    okmask = 0u;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * kThreads;
+      const int kgi = c % KG, dc = c / KG;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = k0 + kgi * 4 + rr;
+        const bool ok = (TOTAL % kThreads == 0 || c < TOTAL) && (key < Lkv) && (dc * 8 < d);
+        r[it][rr] = ldg16(ok ? vg + (size_t)key * d + dc * 8 : vg);
+        okmask |= ok ? (1u << (4 * it + rr)) : 0u;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* Vt, int tid) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * kThreads;
+      if (TOTAL % kThreads == 0 || c < TOTAL) {
+        const int kgi = c % KG, dc = c / KG;
+        u16x8 rows[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          rows[rr] = __builtin_bit_cast(
+              u16x8, ((okmask >> (4 * it + rr)) & 1u) ? r[it][rr] : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u16x4 col = {rows[0][i], rows[1][i], rows[2][i], rows[3][i]};
+          *reinterpret_cast<u16x4*>(Vt + (dc * 8 + i) * VP + kgi * 4) = col;
+        }
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // One wave, NQB query blocks of 16 rows, NK32 steps of 32 keys starting at
@@ -369,12 +446,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(KernelArgs a) {
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  KTile<KEYS, DQK> kt;
+  VtTile<KEYS, DV> vt;
+  kt.load(kg, t_begin * KEYS, a.Lkv, d, tid);
+  vt.load(vg, t_begin * KEYS, a.Lkv, d, tid);
   for (int t = t_begin; t < t_end; ++t) {
     const int k0 = t * KEYS;
     __syncthreads();
-    stage_k<KEYS, DQK>(Ks, kg, k0, a.Lkv, d, tid);
-    stage_vt<KEYS, DV>(Vt, vg, k0, a.Lkv, d, tid);
+    kt.store(Ks, tid);
+    vt.store(Vt, tid);
     __syncthreads();
+    if (t + 1 < t_end) {
+      kt.load(kg, k0 + KEYS, a.Lkv, d, tid);
+      vt.load(vg, k0 + KEYS, a.Lkv, d, tid);
+    }
     bool full = k0 + KEYS <= a.Lkv;
     if (a.causal) full = full && (k0 + KEYS - 1 <= pos_min);
     if (a.window > 0) {
@@ -450,12 +535,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
   const int pos_min = off, pos_max = off + a.Lq - 1;
   const int t0 = a.t_begin + split * a.tiles_per_split;
   const int t1 = min(a.t_end, t0 + a.tiles_per_split);
+  KTile<KEYS, DQK> kt;
+  VtTile<KEYS, DV> vt;
+  if (t0 < t1) {
+    kt.load(kg, t0 * KEYS, a.Lkv, d, tid);
+    vt.load(vg, t0 * KEYS, a.Lkv, d, tid);
+  }
   for (int t = t0; t < t1; ++t) {
     const int k0 = t * KEYS;
     __syncthreads();
-    stage_k<KEYS, DQK>(Ks, kg, k0, a.Lkv, d, tid);
-    stage_vt<KEYS, DV>(Vt, vg, k0, a.Lkv, d, tid);
+    kt.store(Ks, tid);
+    vt.store(Vt, tid);
     __syncthreads();
+    if (t + 1 < t1) {
+      kt.load(kg, k0 + KEYS, a.Lkv, d, tid);
+      vt.load(vg, k0 + KEYS, a.Lkv, d, tid);
+    }
     // Full-tile test on this wave's 32 keys.
     const int w0 = k0 + 32 * wave;
     bool full = w0 + 32 <= a.Lkv;
@@ -483,89 +578,118 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
     for (int i = 0; i < 4; ++i) wo[wave][c16 * OP + 16 * db + 4 * g4 + i] = o[0][db][i];
   __syncthreads();
 
-  // Thread -> (row rr, 8-column chunk cc); 16 rows x DV*2 chunks <= 256.
-  const int rr = tid / (DV * 2), cc = tid % (DV * 2);
-  const bool active = (tid < 16 * DV * 2) && (rr < a.nrows);
-  float M = kNegInf, L = 0.f, acc[8];
+  // Thread -> float4 chunks q = tid + 256*j of the [nrows][DVP] output block:
+  // row q / CPR, columns 4*(q % CPR) .. +3, so a wave touches contiguous memory.
+  constexpr int CPR = DVP / 4;
+  constexpr int JN = (16 * CPR + kThreads - 1) / kThreads;
+  const int nch = a.nrows * CPR;
+  float M[JN], L[JN];
+  f32x4 acc[JN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (active) {
+  for (int j = 0; j < JN; ++j) {
+    const int q = tid + j * kThreads;
+    const int row = min(q / CPR, 15), c4 = q % CPR;
+    M[j] = kNegInf;
+    L[j] = 0.f;
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][rr]);
-    if (M != kNegInf) {
+    for (int w = 0; w < 4; ++w) M[j] = fmaxf(M[j], wm[w][row]);
+    if (M[j] != kNegInf) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float f = fast_exp2(wm[w][rr] - M);
-        L += f * wl[w][rr];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += f * wo[w][rr * OP + cc * 8 + i];
+        const float f = fast_exp2(wm[w][row] - M[j]);
+        L[j] += f * wl[w][row];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&wo[w][row * OP + 4 * c4]);
+        acc[j] += f * x;
       }
     }
   }
 
   if (a.nsplit == 1) {
-    if (active && cc * 8 < d) {
-      const float inv = 1.0f / L;
-      const size_t oo = (((size_t)b * a.Hq + kvh * G + rr % G) * a.Lq + rr / G) * d + cc * 8;
-      u32x4 w = {Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv),
-                 Elem<T>::pack2(acc[4] * inv, acc[5] * inv), Elem<T>::pack2(acc[6] * inv, acc[7] * inv)};
-      *reinterpret_cast<u32x4*>(og + oo) = w;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+      const int q = tid + j * kThreads;
+      const int row = q / CPR, c4 = q % CPR;
+      if (q < nch && 4 * c4 < d) {
+        const float inv = 1.0f / L[j];
+        const size_t oo = (((size_t)b * a.Hq + kvh * G + row % G) * a.Lq + row / G) * d + 4 * c4;
+        *reinterpret_cast<u32x2*>(og + oo) =
+            u32x2{Elem<T>::pack2(acc[j][0] * inv, acc[j][1] * inv), Elem<T>::pack2(acc[j][2] * inv, acc[j][3] * inv)};
+      }
     }
     return;
   }
 
-  // ---- write this split's partial ----------------------------------------------
-  const size_t pidx = ((size_t)unit * a.nsplit + split) * a.nrows;
-  if (active) {
-    float* po = a.ws_o + (pidx + rr) * DVP + cc * 8;
-    *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    if (cc == 0) {
-      a.ws_ml[(pidx + rr) * 2 + 0] = M;
-      a.ws_ml[(pidx + rr) * 2 + 1] = L;
+  // ---- write this split's partial (device-coherent stores) -----------------------
+  const uint32_t o_bytes = (uint32_t)gridDim.x * a.nrows * DVP * 4;
+  const uint32_t ml_bytes = (uint32_t)gridDim.x * a.nrows * 8;
+  const auto rs_o = make_rsrc(a.ws_o, o_bytes);
+  const auto rs_ml = make_rsrc(a.ws_ml, ml_bytes);
+  const int pidx = (unit * a.nsplit + split) * a.nrows;
+#pragma unroll
+  for (int j = 0; j < JN; ++j) {
+    const int q = tid + j * kThreads;
+    const int row = q / CPR, c4 = q % CPR;
+    if (q < nch) {
+      st_dev16(rs_o, ((pidx + row) * DVP + 4 * c4) * 4, acc[j]);
+      if (c4 == 0) st_dev8(rs_ml, (pidx + row) * 8, f32x2{M[j], L[j]});
     }
   }
-  __threadfence();
+  wait_vmem_done();
   __syncthreads();
   if (tid == 0) {
     const unsigned prev =
-        __hip_atomic_fetch_add(a.ws_cnt + unit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.ws_cnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == (unsigned)(a.nsplit - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
 
-  // ---- last arrival: merge all splits in split order -------------------------------
-  if (active) {
-    const size_t base = (size_t)unit * a.nsplit * a.nrows;
-    float Mg = kNegInf;
-    for (int s = 0; s < a.nsplit; ++s)
-      Mg = fmaxf(Mg, __builtin_nontemporal_load(a.ws_ml + (base + (size_t)s * a.nrows + rr) * 2));
-    float Lg = 0.f, og8[8];
+  // ---- last arrival: merge all splits in split order ---------------------------------
+  // Online merge over groups of 8 splits; every load of a group is issued
+  // before any of them is used.
+  constexpr int CHUNK = 8;
+  const int base = unit * a.nsplit * a.nrows;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) og8[i] = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const size_t pr = base + (size_t)s * a.nrows + rr;
-      const float ms = __builtin_nontemporal_load(a.ws_ml + pr * 2);
-      if (ms == kNegInf) continue;
-      const float f = fast_exp2(ms - Mg);
-      Lg += f * __builtin_nontemporal_load(a.ws_ml + pr * 2 + 1);
-      const float* po = a.ws_o + pr * DVP + cc * 8;
-      const f32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po));
-      const f32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 4));
+  for (int j = 0; j < JN; ++j) {
+    const int q = tid + j * kThreads;
+    if (q >= nch) continue;
+    const int row = q / CPR, c4 = q % CPR;
+    float Mg = kNegInf, Lg = 0.f;
+    f32x4 og4 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.nsplit; s0 += CHUNK) {
+      f32x2 ml[CHUNK];
+      f32x4 x[CHUNK];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        og8[i] += f * x0[i];
-        og8[4 + i] += f * x1[i];
+      for (int jj = 0; jj < CHUNK; ++jj) {
+        const int sp = min(s0 + jj, a.nsplit - 1);
+        const int pr = base + sp * a.nrows + row;
+        ml[jj] = ld_dev8(rs_ml, pr * 8);
+        x[jj] = ld_dev16(rs_o, (pr * DVP + 4 * c4) * 4);
+      }
+      float mc = Mg;
+#pragma unroll
+      for (int jj = 0; jj < CHUNK; ++jj)
+        if (s0 + jj < a.nsplit) mc = fmaxf(mc, ml[jj][0]);
+      // No branch here, so the compiler can keep all loads of a group in flight.
+      const bool any = mc != kNegInf;
+      const float fr = any ? fast_exp2(Mg - mc) : 1.f;  // 0 while nothing was merged yet
+      Lg *= fr;
+      og4 *= fr;
+      Mg = any ? mc : Mg;
+#pragma unroll
+      for (int jj = 0; jj < CHUNK; ++jj) {
+        const float f =
+            (s0 + jj < a.nsplit && ml[jj][0] != kNegInf) ? fast_exp2(ml[jj][0] - Mg) : 0.f;
+        Lg += f * ml[jj][1];
+        og4 += f * x[jj];
       }
     }
-    if (cc * 8 < d) {
+    if (4 * c4 < d) {
       const float inv = 1.0f / Lg;
-      const size_t oo = (((size_t)b * a.Hq + kvh * G + rr % G) * a.Lq + rr / G) * d + cc * 8;
-      u32x4 w = {Elem<T>::pack2(og8[0] * inv, og8[1] * inv), Elem<T>::pack2(og8[2] * inv, og8[3] * inv),
-                 Elem<T>::pack2(og8[4] * inv, og8[5] * inv), Elem<T>::pack2(og8[6] * inv, og8[7] * inv)};
-      *reinterpret_cast<u32x4*>(og + oo) = w;
+      const size_t oo = (((size_t)b * a.Hq + kvh * G + row % G) * a.Lq + row / G) * d + 4 * c4;
+      *reinterpret_cast<u32x2*>(og + oo) =
+          u32x2{Elem<T>::pack2(og4[0] * inv, og4[1] * inv), Elem<T>::pack2(og4[2] * inv, og4[3] * inv)};
     }
   }
   if (tid == 0) __hip_atomic_store(a.ws_cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
