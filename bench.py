@@ -34,6 +34,7 @@ METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 MFMA
 LLC_BYTES = 256 * 1024 * 1024    # MI355X last-level (Infinity) cache
+COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate byte counters
 KERNEL_SRC = os.path.join(ROOT, "masked_gqa_attention_amd", "csrc", "mgqa_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_decode_gqa4_kv8192.json")
 
@@ -154,7 +155,8 @@ def cpu_baseline(runner, gpu_out):
     times = []
     t_total = time.perf_counter()
     ref = None
-    while len(times) < 5 and (time.perf_counter() - t_total) < 20.0:
+    # Repeat the whole-input oracle until about 10 s of CPU work (3 runs at least).
+    while len(times) < 3 or (time.perf_counter() - t_total) < 10.0:
         t0 = time.perf_counter()
         ref = oracle.attention(qf, kf, vf, w.causal, w.window, w.softcap)
         times.append(time.perf_counter() - t0)
@@ -165,7 +167,7 @@ def cpu_baseline(runner, gpu_out):
     return {
         "value": wk["bytes"] / t / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
         "sample": f"whole {w.name} input ({w.B * w.Hq * w.Lq} query rows x {w.Lkv} keys), "
-                  f"median of {len(times)} runs, {t:.3f} s each",
+                  f"median of {len(times)} runs of {t:.3f} s ({time.perf_counter() - t_total:.1f} s in all)",
         "seconds": t, "parity_vs_gpu": {"ok": ok, "max_abs_err": float(err.max())},
     }
 
@@ -193,6 +195,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads to measure besides the headline, or 'all'/'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy 5 times (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -244,6 +249,16 @@ def main(argv=None) -> int:
             del r
             torch.cuda.empty_cache()
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 x {COPY_BYTES} bytes read + written")
+        del src, dst
+
     r, ms, steps, fig = headline
     w = r.w
     gpu_out = r.output_f64((steps - 1) % len(r.outs))
@@ -271,6 +286,7 @@ def main(argv=None) -> int:
         "workloads": {n: {k: v for k, v in res.items() if k not in ("shape",)}
                       for n, res in results.items()},
         "device": torch.cuda.get_device_name(0),
+        "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
         "torch": torch.__version__,
         "hip": torch.version.hip,
     }
