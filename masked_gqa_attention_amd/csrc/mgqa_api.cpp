@@ -84,19 +84,17 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
     p.path = kPathPrefill;
     p.keys_per_tile = kPrefillKeys;
     p.nsplit = 1;
-    // Largest query block that still gives at least two workgroups per CU;
-    // the smallest block otherwise.
-    int nqb = 1;
-    for (int cand = 4; cand >= 1; cand /= 2) {
-      const int m = 64 * cand / G;
-      const long long wgs = units * ((Lq + m - 1) / m);
-      if (wgs >= 2 * kCUs) {
-        nqb = cand;
-        break;
-      }
+    // 8 waves x 32 rows (256 rows per workgroup) when that still gives at
+    // least two workgroups per CU, else 4 waves x 16 rows.
+    const int m_big = 256 / G;
+    const long long wgs_big = units * ((Lq + m_big - 1) / m_big);
+    if (wgs_big >= 2 * kCUs) {
+      p.nqb = 2;
+      p.rows_per_wg = 256;
+    } else {
+      p.nqb = 1;
+      p.rows_per_wg = 64;
     }
-    p.nqb = nqb;
-    p.rows_per_wg = 64 * nqb;
     const int m = p.rows_per_wg / G;
     p.workgroups = units * ((Lq + m - 1) / m);
   }

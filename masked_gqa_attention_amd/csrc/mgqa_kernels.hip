@@ -381,20 +381,187 @@ __device__ __forceinline__ void store_row(uint16_t* orow, const f32x4 (&o)[DV], 
 }
 
 // ---------------------------------------------------------------------------
-// Prefill / encoder kernel: one workgroup per (batch, kv head, block of m
-// query positions); 4 waves x NQB x 16 rows; rows are (head of the group,
-// position) pairs with the head index fastest.
+// Prefill path.  K and V tiles are both staged row-major ([key][head size],
+// rows padded); V is read transposed straight from LDS with
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j%4
+// of the 8-byte rows addressed by lanes 4e + j/4 (e = 0..3).  Pointing lane s
+// at row key0 + s/4, columns c0 + 4*(s%4) .. +3 therefore hands lane j the
+// four keys key0..key0+3 of column c0 + j: the A-operand slice of V^T.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NQB, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(KernelArgs a) {
+
+// Row-major tile [KEYS][PITCH] of 16-bit elements moved by NT threads in
+// 16-byte chunks, CH chunks per row; rows past Lkv and chunks past d are zero.
+template <int KEYS, int CH, int PITCH, int NT>
+struct RowTile {
+  static constexpr int TOTAL = KEYS * CH;
+  static constexpr int PER = (TOTAL + NT - 1) / NT;
+  u32x4 r[PER];
+  uint32_t okmask;
+
+  __device__ __forceinline__ void load(const uint16_t* g, int k0, int Lkv, int d, int tid) {
+    okmask = 0u;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * NT;
+      const int key = c / CH, ch = c % CH;
+      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (k0 + key < Lkv) && (ch * 8 < d);
+      r[it] = ldg16(ok ? g + (size_t)(k0 + key) * d + ch * 8 : g);
+      okmask |= ok ? (1u << it) : 0u;
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* sm, int tid) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * NT;
+      if (TOTAL % NT == 0 || c < TOTAL)
+        *reinterpret_cast<u32x4*>(sm + (c / CH) * PITCH + (c % CH) * 8) =
+            ((okmask >> it) & 1u) ? r[it] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed 4-key x 1-column read (see above); returns the 4 keys of this
+// lane's column as two packed dwords.
+__device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// One wave, NQB query blocks of 16 rows, NK32 steps of 32 keys from tile-local
+// key kbase, natural key order: S^T block (step tt, half hh) row rho is key
+// kbase + 32*tt + 16*hh + rho, so lane group g4 holds keys 32*tt + 4*g4 + i
+// (hh = 0) and 32*tt + 16 + 4*g4 + i (hh = 1): the P^T operand of step tt.
+template <typename T, int DQK, int DV, int NQB, int NK32, int KP, int VP, bool SOFTCAP>
+__device__ __forceinline__ void wave_step_tr(const uint16_t* Ks, const uint16_t* Vs, int kbase,
+                                             int kglob0, bool full, const u32x4 (&qf)[NQB][DQK],
+                                             const int (&qpos)[NQB], float (&m_e)[NQB],
+                                             float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                             const KernelArgs& a, int lane) {
+  const int c16 = lane & 15, g4 = lane >> 4;
+
+  f32x4 s[NQB][NK32][2];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) s[qb][tt][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint16_t* krow = Ks + (kbase + 32 * tt + 16 * hh + c16) * KP + 8 * g4;
+#pragma unroll
+      for (int t = 0; t < DQK; ++t) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 32 * t);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][tt][hh] = Elem<T>::mfma(kf, qf[qb][t], s[qb][tt][hh]);
+      }
+    }
+
+  u32x4 pk[NQB][NK32];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (!full) {
+#pragma unroll
+      for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = kglob0 + kbase + 32 * tt + 16 * hh + 4 * g4 + i;
+            if (!key_visible(j, qpos[qb], a.Lkv, a.causal, a.window)) s[qb][tt][hh][i] = kNegInf;
+          }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < NK32; ++tt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][tt][hh][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mxe;
+    if (SOFTCAP) {
+      // Same formula as the per-score path below, so the row maximum maps to
+      // exactly 2^0 before any rescale slack.
+      mxe = (mx == kNegInf) ? kNegInf
+                            : __builtin_fmaf(fast_rcp(fast_exp2(mx * a.gamma) + 1.0f), -2.0f * a.c2, a.c2);
+    } else {
+      mxe = mx * a.alpha;
+    }
+    if (mxe > m_e[qb] + kRescaleSlack) {
+      const float f = fast_exp2(m_e[qb] - mxe);  // 0 when m_e was -inf
+      m_e[qb] = mxe;
+      l_p[qb] *= f;
+#pragma unroll
+      for (int db = 0; db < DV; ++db) o[qb][db] *= f;
+    }
+    const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
+    float lsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NK32; ++tt) {
+      float p[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = s[qb][tt][hh][i];
+          float pv;
+          if (SOFTCAP) {
+            const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
+            pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
+            if (!full && x == kNegInf) pv = 0.f;
+          } else {
+            pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
+          }
+          p[hh * 4 + i] = pv;
+          lsum += pv;
+        }
+      pk[qb][tt] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
+                         Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
+    }
+    l_p[qb] += lsum;
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < NK32; ++tt) {
+    const uint16_t* v0 = Vs + (kbase + 32 * tt + 4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3);
+    const uint16_t* v1 = v0 + 16 * VP;
+#pragma unroll
+    for (int db = 0; db < DV; ++db) {
+      const u32x2 lo = lds_read_tr4(v0 + 16 * db);
+      const u32x2 hi = lds_read_tr4(v1 + 16 * db);
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[qb][tt], o[qb][db]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / encoder kernel: one workgroup per (batch, kv head, block of m
+// query positions); NWAVES waves x NQB x 16 rows; rows are (head of the group,
+// position) pairs with the head index fastest.  Two LDS stages: while every
+// wave works on one tile, the next tile's loads are in flight in registers and
+// are written to the other stage right after, so one barrier per tile.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, int NQB, int NWAVES, bool SOFTCAP>
+__global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
+  constexpr int NT = NWAVES * 64;
   constexpr int KEYS = kPrefillKeys;
-  constexpr int KP = DQK * 32 + 8;
-  constexpr int VP = KEYS + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KEYS * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * 16 * VP];
+  constexpr int KP = DQK * 32 + 8;   // 16 rows of a K read land on distinct banks
+  constexpr int VP = DV * 16 + 16;   // 4 rows x 32 B of a transposed V read do too
+  constexpr int STAGE = KEYS * (KP + VP);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, g4 = lane >> 4;
+  const int g4 = lane >> 4, c16 = lane & 15;
 
   const int bid = blockIdx.x;
   const int pblk = bid % a.n_pos_blk;
@@ -446,16 +613,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(KernelArgs a) {
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  KTile<KEYS, DQK> kt;
-  VtTile<KEYS, DV> vt;
+  RowTile<KEYS, DQK * 4, KP, NT> kt;
+  RowTile<KEYS, DV * 2, VP, NT> vt;
   kt.load(kg, t_begin * KEYS, a.Lkv, d, tid);
   vt.load(vg, t_begin * KEYS, a.Lkv, d, tid);
+  kt.store(smem, tid);
+  vt.store(smem + KEYS * KP, tid);
+  __syncthreads();
   for (int t = t_begin; t < t_end; ++t) {
     const int k0 = t * KEYS;
-    __syncthreads();
-    kt.store(Ks, tid);
-    vt.store(Vt, tid);
-    __syncthreads();
+    const int cur = (t - t_begin) & 1;
+    const uint16_t* Ks = smem + cur * STAGE;
+    const uint16_t* Vs = Ks + KEYS * KP;
     if (t + 1 < t_end) {
       kt.load(kg, k0 + KEYS, a.Lkv, d, tid);
       vt.load(vg, k0 + KEYS, a.Lkv, d, tid);
@@ -466,8 +635,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(KernelArgs a) {
       full = full && (pos_max - k0 < a.window);
       if (!a.causal) full = full && (k0 + KEYS - 1 - pos_min < a.window);
     }
-    wave_step<T, DQK, DV, NQB, KEYS / 32, KEYS, SOFTCAP>(Ks, Vt, 0, k0, full, qf, qpos, m_e, l_p,
-                                                          o, a, lane);
+    wave_step_tr<T, DQK, DV, NQB, KEYS / 32, KP, VP, SOFTCAP>(Ks, Vs, 0, k0, full, qf, qpos, m_e,
+                                                               l_p, o, a, lane);
+    if (t + 1 < t_end) {
+      uint16_t* nxt = smem + (cur ^ 1) * STAGE;
+      kt.store(nxt, tid);
+      vt.store(nxt + KEYS * KP, tid);
+    }
+    __syncthreads();
   }
 
 #pragma unroll
@@ -709,12 +884,10 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathDecode) {
     hipLaunchKernelGGL((decode_kernel<T, DQK, DV, SOFTCAP>), grid, block, 0, st, args);
-  } else if (plan.nqb == 4) {
-    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 4, SOFTCAP>), grid, block, 0, st, args);
   } else if (plan.nqb == 2) {
-    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, SOFTCAP>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 1, SOFTCAP>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 1, 4, SOFTCAP>), grid, block, 0, st, args);
   }
   return hipGetLastError();
 }
