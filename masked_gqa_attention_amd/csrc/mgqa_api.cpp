@@ -17,6 +17,14 @@ constexpr int kCUs = 256;              // MI355X compute units
 #ifndef MGQA_DECODE_TARGET_WGS
 #define MGQA_DECODE_TARGET_WGS 512
 #endif
+// Prefill block shape (waves per workgroup, 16-row blocks per wave); the
+// kernels are instantiated for 4x1 and 8x2.
+#ifndef MGQA_PREFILL_WAVES
+#define MGQA_PREFILL_WAVES 8
+#endif
+#ifndef MGQA_PREFILL_NQB
+#define MGQA_PREFILL_NQB 2
+#endif
 // Decode: split the key band until about this many workgroups run (two per CU).
 constexpr long long kTargetWGs = MGQA_DECODE_TARGET_WGS;
 
@@ -84,17 +92,20 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
     p.path = kPathPrefill;
     p.keys_per_tile = kPrefillKeys;
     p.nsplit = 1;
-    // 8 waves x 32 rows (256 rows per workgroup) when that still gives at
-    // least two workgroups per CU, else 4 waves x 16 rows.
-    const int m_big = 256 / G;
+    // The large block (MGQA_PREFILL_WAVES waves x MGQA_PREFILL_NQB 16-row
+    // blocks) when it still gives at least two workgroups per CU, else
+    // 4 waves x 16 rows.
+    const int big_rows = 16 * MGQA_PREFILL_WAVES * MGQA_PREFILL_NQB;
+    const int m_big = big_rows / G;
     const long long wgs_big = units * ((Lq + m_big - 1) / m_big);
     if (wgs_big >= 2 * kCUs) {
-      p.nqb = 2;
-      p.rows_per_wg = 256;
+      p.nqb = MGQA_PREFILL_NQB;
+      p.nwaves = MGQA_PREFILL_WAVES;
     } else {
       p.nqb = 1;
-      p.rows_per_wg = 64;
+      p.nwaves = 4;
     }
+    p.rows_per_wg = 16 * p.nwaves * p.nqb;
     const int m = p.rows_per_wg / G;
     p.workgroups = units * ((Lq + m - 1) / m);
   }

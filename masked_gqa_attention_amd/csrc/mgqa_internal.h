@@ -46,6 +46,7 @@ struct Plan {
   int dqk;            // 32-wide head-size steps for Q.K^T
   int dv;             // 16-wide head-size blocks for P.V
   int nqb;            // prefill: 16-row query blocks per wave
+  int nwaves;         // prefill: waves per workgroup
   int rows_per_wg;
   int keys_per_tile;
   int nsplit;

@@ -390,32 +390,39 @@ __device__ __forceinline__ void store_row(uint16_t* orow, const f32x4 (&o)[DV], 
 // ---------------------------------------------------------------------------
 
 // Row-major tile [KEYS][PITCH] of 16-bit elements moved by NT threads in
-// 16-byte chunks, CH chunks per row; rows past Lkv and chunks past d are zero.
+// 16-byte chunks, CH chunks per row.  Loads are raw buffer loads through a
+// descriptor based at the tile's first key whose range ends at Lkv, so keys
+// past Lkv read as zero in hardware; chunks past d get an offset beyond any
+// range and read as zero too.  Per-thread offsets are loop invariant.
 template <int KEYS, int CH, int PITCH, int NT>
 struct RowTile {
   static constexpr int TOTAL = KEYS * CH;
   static constexpr int PER = (TOTAL + NT - 1) / NT;
   u32x4 r[PER];
-  uint32_t okmask;
+  int voff[PER];
 
-  __device__ __forceinline__ void load(const uint16_t* g, int k0, int Lkv, int d, int tid) {
-    okmask = 0u;
+  __device__ __forceinline__ void init(int d, int tid) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
       const int c = tid + it * NT;
       const int key = c / CH, ch = c % CH;
-      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (k0 + key < Lkv) && (ch * 8 < d);
-      r[it] = ldg16(ok ? g + (size_t)(k0 + key) * d + ch * 8 : g);
-      okmask |= ok ? (1u << it) : 0u;
+      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (ch * 8 < d);
+      voff[it] = ok ? (key * d + ch * 8) * 2 : 0x7FFFFFF0;
     }
+  }
+  // g: the (batch, kv head) unit's first row; loads keys k0 .. k0+KEYS-1.
+  __device__ __forceinline__ void load(const uint16_t* g, int k0, int Lkv, int d) {
+    const auto rs = make_rsrc(g + (size_t)k0 * d, (uint32_t)(Lkv - k0) * (uint32_t)d * 2u);
+#pragma unroll
+    for (int it = 0; it < PER; ++it)
+      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[it], 0, 0));
   }
   __device__ __forceinline__ void store(uint16_t* sm, int tid) const {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
       const int c = tid + it * NT;
       if (TOTAL % NT == 0 || c < TOTAL)
-        *reinterpret_cast<u32x4*>(sm + (c / CH) * PITCH + (c % CH) * 8) =
-            ((okmask >> it) & 1u) ? r[it] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm + (c / CH) * PITCH + (c % CH) * 8) = r[it];
     }
   }
 };
@@ -434,9 +441,9 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
 // key kbase, natural key order: S^T block (step tt, half hh) row rho is key
 // kbase + 32*tt + 16*hh + rho, so lane group g4 holds keys 32*tt + 4*g4 + i
 // (hh = 0) and 32*tt + 16 + 4*g4 + i (hh = 1): the P^T operand of step tt.
-template <typename T, int DQK, int DV, int NQB, int NK32, int KP, int VP, bool SOFTCAP>
+template <typename T, int DQK, int DV, int NQB, int NK32, int KP, int VP, bool SOFTCAP, bool MASK>
 __device__ __forceinline__ void wave_step_tr(const uint16_t* Ks, const uint16_t* Vs, int kbase,
-                                             int kglob0, bool full, const u32x4 (&qf)[NQB][DQK],
+                                             int kglob0, const u32x4 (&qf)[NQB][DQK],
                                              const int (&qpos)[NQB], float (&m_e)[NQB],
                                              float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
                                              const KernelArgs& a, int lane) {
@@ -466,7 +473,7 @@ __device__ __forceinline__ void wave_step_tr(const uint16_t* Ks, const uint16_t*
   u32x4 pk[NQB][NK32];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    if (!full) {
+    if (MASK) {
 #pragma unroll
       for (int tt = 0; tt < NK32; ++tt)
 #pragma unroll
@@ -516,7 +523,7 @@ __device__ __forceinline__ void wave_step_tr(const uint16_t* Ks, const uint16_t*
           if (SOFTCAP) {
             const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
             pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
-            if (!full && x == kNegInf) pv = 0.f;
+            if (MASK && x == kNegInf) pv = 0.f;
           } else {
             pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
           }
@@ -615,8 +622,10 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 
   RowTile<KEYS, DQK * 4, KP, NT> kt;
   RowTile<KEYS, DV * 2, VP, NT> vt;
-  kt.load(kg, t_begin * KEYS, a.Lkv, d, tid);
-  vt.load(vg, t_begin * KEYS, a.Lkv, d, tid);
+  kt.init(d, tid);
+  vt.init(d, tid);
+  kt.load(kg, t_begin * KEYS, a.Lkv, d);
+  vt.load(vg, t_begin * KEYS, a.Lkv, d);
   kt.store(smem, tid);
   vt.store(smem + KEYS * KP, tid);
   __syncthreads();
@@ -626,8 +635,8 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
     const uint16_t* Ks = smem + cur * STAGE;
     const uint16_t* Vs = Ks + KEYS * KP;
     if (t + 1 < t_end) {
-      kt.load(kg, k0 + KEYS, a.Lkv, d, tid);
-      vt.load(vg, k0 + KEYS, a.Lkv, d, tid);
+      kt.load(kg, k0 + KEYS, a.Lkv, d);
+      vt.load(vg, k0 + KEYS, a.Lkv, d);
     }
     bool full = k0 + KEYS <= a.Lkv;
     if (a.causal) full = full && (k0 + KEYS - 1 <= pos_min);
@@ -635,8 +644,16 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
       full = full && (pos_max - k0 < a.window);
       if (!a.causal) full = full && (k0 + KEYS - 1 - pos_min < a.window);
     }
-    wave_step_tr<T, DQK, DV, NQB, KEYS / 32, KP, VP, SOFTCAP>(Ks, Vs, 0, k0, full, qf, qpos, m_e,
-                                                               l_p, o, a, lane);
+    // 32-key steps keep the score registers small.
+#pragma unroll
+    for (int kb = 0; kb < KEYS; kb += 32) {
+      if (full)
+        wave_step_tr<T, DQK, DV, NQB, 1, KP, VP, SOFTCAP, false>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o,
+                                                                  a, lane);
+      else
+        wave_step_tr<T, DQK, DV, NQB, 1, KP, VP, SOFTCAP, true>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o,
+                                                                 a, lane);
+    }
     if (t + 1 < t_end) {
       uint16_t* nxt = smem + (cur ^ 1) * STAGE;
       kt.store(nxt, tid);
@@ -884,7 +901,7 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathDecode) {
     hipLaunchKernelGGL((decode_kernel<T, DQK, DV, SOFTCAP>), grid, block, 0, st, args);
-  } else if (plan.nqb == 2) {
+  } else if (plan.nwaves == 8 && plan.nqb == 2) {
     hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 1, 4, SOFTCAP>), grid, block, 0, st, args);
