@@ -50,6 +50,9 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
+#ifndef MGQA_EARLY_FRAG
+#define MGQA_EARLY_FRAG false
+#endif
 // Lazy rescale threshold in base-2 exponent units.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -430,6 +433,15 @@ struct RowTile {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// 16-byte buffer load per lane that writes LDS directly: lane l's bytes land
+// at lds + 16*l (the base must be the same for the whole wave).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0,
+                                           0, 0);
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Transposed 4-key x 1-column read (see above); returns the 4 keys of this
 // lane's column as two packed dwords.
 __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
@@ -437,60 +449,136 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// One wave, NQB query blocks of 16 rows, NK32 steps of 32 keys from tile-local
-// key kbase, natural key order: S^T block (step tt, half hh) row rho is key
-// kbase + 32*tt + 16*hh + rho, so lane group g4 holds keys 32*tt + 4*g4 + i
-// (hh = 0) and 32*tt + 16 + 4*g4 + i (hh = 1): the P^T operand of step tt.
-template <typename T, int DQK, int DV, int NQB, int NK32, int KP, int VP, bool SOFTCAP, bool MASK>
-__device__ __forceinline__ void wave_step_tr(const uint16_t* Ks, const uint16_t* Vs, int kbase,
-                                             int kglob0, const u32x4 (&qf)[NQB][DQK],
-                                             const int (&qpos)[NQB], float (&m_e)[NQB],
-                                             float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
-                                             const KernelArgs& a, int lane) {
-  const int c16 = lane & 15, g4 = lane >> 4;
+// Prefill per-wave tile work.  A step is 32 keys: S^T blocks hh = 0, 1 of 16
+// keys each, natural key order (block row rho is key kbase + 16*hh + rho), so
+// lane group g4 holds keys 4*g4 + i (hh = 0) and 16 + 4*g4 + i (hh = 1): the
+// P^T operand that the transposed V reads above produce.  LDS fragments are
+// read one phase ahead of their use -- V for the step before the softmax
+// arithmetic, K for the next step before the P.V products -- so LDS latency
+// overlaps other work.
 
-  f32x4 s[NQB][NK32][2];
+// Two LDS tile layouts.  Padded (SWZ = false): rows of KP / VP elements, the
+// padding puts the rows of one read on distinct banks.  Swizzled (SWZ = true,
+// head size 128 only): dense 256-byte rows of sixteen 16-byte slots; chunk c
+// of K row r sits in slot c ^ (r % 16) and chunk c of V row r in slot
+// c ^ 2*(r % 8), which keeps a K-fragment read (16 rows, one chunk) and a
+// transposed V read (4 rows x 2 chunks per 16 lanes) on distinct banks and
+// lets whole rows be written by direct global-to-LDS loads.
+template <int DQK, int KP, bool SWZ>
+__device__ __forceinline__ void read_kfrag(u32x4 (&kf)[2][DQK], const uint16_t* Ks, int kbase, int c16,
+                                           int g4) {
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = kbase + 16 * hh + c16;  // row % 16 == c16
 #pragma unroll
-    for (int tt = 0; tt < NK32; ++tt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) s[qb][tt][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < DQK; ++t) {
+      const uint16_t* p = SWZ ? Ks + row * 128 + (((4 * t + g4) ^ c16) << 3) : Ks + row * KP + 8 * g4 + 32 * t;
+      kf[hh][t] = *reinterpret_cast<const u32x4*>(p);
+    }
+  }
+}
 
+template <int DV, int VP, bool SWZ>
+__device__ __forceinline__ void read_vfrag(u32x4 (&vf)[DV], const uint16_t* Vs, int kbase, int c16,
+                                           int g4) {
+  const int row = kbase + 4 * g4 + (c16 >> 2);
+  const int sw = 2 * ((4 * (g4 & 1) + (c16 >> 2)) & 7);  // 2 * (row % 8)
 #pragma unroll
-  for (int tt = 0; tt < NK32; ++tt)
+  for (int db = 0; db < DV; ++db) {
+    const uint16_t* v0;
+    if (SWZ)
+      v0 = Vs + row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1);
+    else
+      v0 = Vs + row * VP + 4 * (c16 & 3) + 16 * db;
+    const uint16_t* v1 = v0 + 16 * (SWZ ? 128 : VP);
+    const u32x2 lo = lds_read_tr4(v0);
+    const u32x2 hi = lds_read_tr4(v1);
+    vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+// One 32-key step: scores from kf, softcap/mask/online softmax, P.V from V
+// fragments read here.  When NEXT_K, kf is refilled with the fragments of the
+// step at tile-local key kbase + 32 before the P.V products.
+template <int KP, bool SWZ>
+__device__ __forceinline__ u32x4 read_kfrag1(const uint16_t* Ks, int kbase, int hh, int t, int c16,
+                                             int g4) {
+  const int row = kbase + 16 * hh + c16;
+  const uint16_t* p = SWZ ? Ks + row * 128 + (((4 * t + g4) ^ c16) << 3) : Ks + row * KP + 8 * g4 + 32 * t;
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int VP, bool SWZ>
+__device__ __forceinline__ u32x4 read_vfrag1(const uint16_t* Vs, int kbase, int db, int c16, int g4) {
+  const int row = kbase + 4 * g4 + (c16 >> 2);
+  const int sw = 2 * ((4 * (g4 & 1) + (c16 >> 2)) & 7);  // 2 * (row % 8)
+  const uint16_t* v0 = SWZ ? Vs + row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1)
+                           : Vs + row * VP + 4 * (c16 & 3) + 16 * db;
+  const uint16_t* v1 = v0 + 16 * (SWZ ? 128 : VP);
+  const u32x2 lo = lds_read_tr4(v0);
+  const u32x2 hi = lds_read_tr4(v1);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SWZ, bool SOFTCAP, bool MASK,
+          bool NEXT_K, bool EARLY>
+__device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int kbase, int kglob0,
+                                          u32x4 (&kf)[2][DQK], const u32x4 (&qf)[NQB][DQK],
+                                          const int (&qpos)[NQB], float (&m_e)[NQB],
+                                          float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                          const KernelArgs& a, int c16, int g4) {
+  // ---- S^T = K Q^T -------------------------------------------------------
+  f32x4 s[NQB][2];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (EARLY) {
+#pragma unroll
+    for (int t = 0; t < DQK; ++t)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][hh] = Elem<T>::mfma(kf[hh][t], qf[qb][t], s[qb][hh]);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // One fragment at a time: read, then its NQB products.
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const uint16_t* krow = Ks + (kbase + 32 * tt + 16 * hh + c16) * KP + 8 * g4;
+      const uint16_t* krow = Ks + (kbase + 16 * hh + c16) * (SWZ ? 128 : KP);
 #pragma unroll
       for (int t = 0; t < DQK; ++t) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 32 * t);
+        const uint16_t* p = SWZ ? krow + (((4 * t + g4) ^ c16) << 3) : krow + 8 * g4 + 32 * t;
+        const u32x4 k1 = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][tt][hh] = Elem<T>::mfma(kf, qf[qb][t], s[qb][tt][hh]);
+        for (int qb = 0; qb < NQB; ++qb) s[qb][hh] = Elem<T>::mfma(k1, qf[qb][t], s[qb][hh]);
       }
     }
+  }
 
-  u32x4 pk[NQB][NK32];
+  // ---- V fragments for this step (early: in flight during the softmax) ------
+  u32x4 vf[DV];
+  if (EARLY) {
+    read_vfrag<DV, VP, SWZ>(vf, Vs, kbase, c16, g4);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- softcap, mask, online softmax, P^T ------------------------------------
+  u32x4 pk[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     if (MASK) {
 #pragma unroll
-      for (int tt = 0; tt < NK32; ++tt)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = kglob0 + kbase + 32 * tt + 16 * hh + 4 * g4 + i;
-            if (!key_visible(j, qpos[qb], a.Lkv, a.causal, a.window)) s[qb][tt][hh][i] = kNegInf;
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int j = kglob0 + kbase + 16 * hh + 4 * g4 + i;
+          if (!key_visible(j, qpos[qb], a.Lkv, a.causal, a.window)) s[qb][hh][i] = kNegInf;
+        }
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int tt = 0; tt < NK32; ++tt)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][tt][hh][i]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][hh][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float mxe;
@@ -510,43 +598,89 @@ __device__ __forceinline__ void wave_step_tr(const uint16_t* Ks, const uint16_t*
       for (int db = 0; db < DV; ++db) o[qb][db] *= f;
     }
     const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
-    float lsum = 0.f;
+    float p[8];
 #pragma unroll
-    for (int tt = 0; tt < NK32; ++tt) {
-      float p[8];
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = s[qb][tt][hh][i];
-          float pv;
-          if (SOFTCAP) {
-            const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
-            pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
-            if (MASK && x == kNegInf) pv = 0.f;
-          } else {
-            pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
-          }
-          p[hh * 4 + i] = pv;
-          lsum += pv;
+      for (int i = 0; i < 4; ++i) {
+        const float x = s[qb][hh][i];
+        float pv;
+        if (SOFTCAP) {
+          // c*tanh(u) = c - 2c/(exp(2u)+1); in base-2 units the exponent is
+          // c2 - 2*c2*r - mref with r = 1/(2^(x*gamma) + 1).
+          const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
+          pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
+          if (MASK && x == kNegInf) pv = 0.f;
+        } else {
+          pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
         }
-      pk[qb][tt] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
-                         Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
-    }
-    l_p[qb] += lsum;
+        p[hh * 4 + i] = pv;
+      }
+    l_p[qb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    pk[qb] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
+                   Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
   }
+  if (EARLY) __builtin_amdgcn_sched_barrier(0);
 
+  // ---- (early: next step's K fragments), then O^T += V^T P^T -----------------
+  if (EARLY) {
+    if (NEXT_K) read_kfrag<DQK, KP, SWZ>(kf, Ks, kbase + 32, c16, g4);
 #pragma unroll
-  for (int tt = 0; tt < NK32; ++tt) {
-    const uint16_t* v0 = Vs + (kbase + 32 * tt + 4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3);
+    for (int db = 0; db < DV; ++db)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf[db], pk[qb], o[qb][db]);
+    __builtin_amdgcn_sched_barrier(0);
+  } else if (!SWZ) {
+    const uint16_t* v0 = Vs + (kbase + 4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3);
     const uint16_t* v1 = v0 + 16 * VP;
 #pragma unroll
     for (int db = 0; db < DV; ++db) {
       const u32x2 lo = lds_read_tr4(v0 + 16 * db);
       const u32x2 hi = lds_read_tr4(v1 + 16 * db);
-      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      const u32x4 vf1 = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[qb][tt], o[qb][db]);
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf1, pk[qb], o[qb][db]);
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < DV; ++db) {
+      const u32x4 v1 = read_vfrag1<VP, SWZ>(Vs, kbase, db, c16, g4);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(v1, pk[qb], o[qb][db]);
+    }
+  }
+}
+
+// Both 32-key steps of a 64-key tile; the second step's K fragments are read
+// during the first step's products.
+template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SWZ, bool SOFTCAP, bool EARLY>
+__device__ __forceinline__ void tile_pair(const uint16_t* Ks, const uint16_t* Vs, int k0, bool full,
+                                          const u32x4 (&qf)[NQB][DQK], const int (&qpos)[NQB],
+                                          float (&m_e)[NQB], float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                          const KernelArgs& a, int c16, int g4) {
+  u32x4 kf[2][DQK];
+  if (EARLY) {
+    read_kfrag<DQK, KP, SWZ>(kf, Ks, 0, c16, g4);
+    if (full) {
+      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, false, true, true>(Ks, Vs, 0, k0, kf, qf, qpos,
+                                                                          m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, false, false, true>(Ks, Vs, 32, k0, kf, qf, qpos,
+                                                                           m_e, l_p, o, a, c16, g4);
+    } else {
+      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, true, true, true>(Ks, Vs, 0, k0, kf, qf, qpos,
+                                                                         m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, true, false, true>(Ks, Vs, 32, k0, kf, qf, qpos,
+                                                                          m_e, l_p, o, a, c16, g4);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 64; kb += 32) {
+      if (full)
+        tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, false, false, false>(Ks, Vs, kb, k0, kf, qf, qpos,
+                                                                              m_e, l_p, o, a, c16, g4);
+      else
+        tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, true, false, false>(Ks, Vs, kb, k0, kf, qf, qpos,
+                                                                             m_e, l_p, o, a, c16, g4);
     }
   }
 }
@@ -644,16 +778,10 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
       full = full && (pos_max - k0 < a.window);
       if (!a.causal) full = full && (k0 + KEYS - 1 - pos_min < a.window);
     }
-    // 32-key steps keep the score registers small.
-#pragma unroll
-    for (int kb = 0; kb < KEYS; kb += 32) {
-      if (full)
-        wave_step_tr<T, DQK, DV, NQB, 1, KP, VP, SOFTCAP, false>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o,
-                                                                  a, lane);
-      else
-        wave_step_tr<T, DQK, DV, NQB, 1, KP, VP, SOFTCAP, true>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o,
-                                                                 a, lane);
-    }
+    // Two 32-key steps per tile; K fragments of the second step are read
+    // during the first step's products.
+    tile_pair<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, MGQA_EARLY_FRAG>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16,
+                                                        g4);
     if (t + 1 < t_end) {
       uint16_t* nxt = smem + (cur ^ 1) * STAGE;
       kt.store(nxt, tid);
@@ -668,6 +796,144 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, d, g4);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / encoder kernel for head size 128: same work split as
+// prefill_kernel, but K and V tiles go straight from HBM to LDS with buffer
+// loads that write LDS (16 bytes per lane, a wave writes 1 KB = 4 dense rows),
+// through swizzled slots (see read_kfrag).  Keys past Lkv are outside the
+// descriptor's range and land as zeros.  Three LDS stages: tile t+2 is fetched
+// while tile t is in use; one barrier per tile.  No registers or vector ALU
+// work go into staging.
+// ---------------------------------------------------------------------------
+template <typename T, int NQB, int NWAVES, bool SOFTCAP>
+__global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
+  constexpr int DQK = 4, DV = 8, D = 128;
+  constexpr int KEYS = kPrefillKeys;
+  constexpr int TILE = KEYS * D;          // elements of one K (or V) tile
+  constexpr int STAGE = 2 * TILE;
+  constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row DMA instructions per wave per tensor
+  static_assert(IPW * NWAVES * 4 == KEYS, "tile rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int g4 = lane >> 4, c16 = lane & 15;
+
+  const int bid = blockIdx.x;
+  const int pblk = bid % a.n_pos_blk;
+  const int unit = bid / a.n_pos_blk;  // b * Hkv + kvh
+  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int G = a.G;
+  const int q0 = pblk * a.m;
+  const int m_eff = min(a.m, a.Lq - q0);
+  const int off = a.Lkv - a.Lq;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * D;
+  uint16_t* og = static_cast<uint16_t*>(a.out);
+
+  // Key band of this block of positions.
+  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
+  int key_lo = 0, key_hi = a.Lkv - 1;
+  if (a.causal) key_hi = min(key_hi, pos_max);
+  if (a.window > 0) {
+    key_lo = max(0, pos_min - a.window + 1);
+    if (!a.causal) key_hi = min(key_hi, pos_max + a.window - 1);
+  }
+  const int t_begin = key_lo / KEYS, t_end = key_hi / KEYS + 1;
+
+  // DMA lane offsets (bytes from the tile's first key), loop invariant: lane
+  // fills slot lane%16 of row 4*instr + lane/16 with the chunk the swizzle
+  // puts there.
+  int voffK[IPW], voffV[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int row = 4 * (wave * IPW + j) + (lane >> 4), slot = lane & 15;
+    voffK[j] = (row * D + ((slot ^ (row & 15)) << 3)) * 2;
+    voffV[j] = (row * D + ((slot ^ (2 * (row & 7))) << 3)) * 2;
+  }
+  auto fetch = [&](int t, int st) {
+    const int k0 = t * KEYS;
+    const uint32_t bytes = (uint32_t)(a.Lkv - k0) * (uint32_t)(D * 2);
+    const auto rk = make_rsrc(kg + (size_t)k0 * D, bytes);
+    const auto rv = make_rsrc(vg + (size_t)k0 * D, bytes);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      uint16_t* dk = smem + st * STAGE + (wave * IPW + j) * 4 * D;
+      lds_dma16(rk, dk, voffK[j]);
+      lds_dma16(rv, dk + TILE, voffV[j]);
+    }
+  };
+
+  fetch(t_begin, 0);
+  if (t_begin + 1 < t_end) fetch(t_begin + 1, 1);
+
+  u32x4 qf[NQB][DQK];
+  int qpos[NQB];
+  bool rok[NQB];
+  size_t roff[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int r = (wave * NQB + qb) * 16 + c16;
+    const int pl = r / G, hr = r % G;
+    rok[qb] = pl < m_eff;
+    const int pos = q0 + pl;
+    qpos[qb] = pos + off;
+    const int head = kvh * G + hr;
+    roff[qb] = (((size_t)b * a.Hq + head) * a.Lq + (rok[qb] ? pos : 0)) * D;
+    load_q<DQK>(qf[qb], qg + roff[qb], rok[qb], D, g4);
+  }
+
+  float m_e[NQB], l_p[NQB];
+  f32x4 o[NQB][DV];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_e[qb] = kNegInf;
+    l_p[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  int sc = 0;  // LDS stage of tile t
+  for (int t = t_begin; t < t_end; ++t) {
+    // This wave's loads of tile t are done once at most the next tile's
+    // 2*IPW loads are still outstanding; the barrier publishes every wave's.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (t + 1 < t_end) {
+      if constexpr (IPW == 2)
+        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    // Every wave is past tile t-1, so its stage takes tile t+2.
+    if (t + 2 < t_end) fetch(t + 2, sc == 0 ? 2 : sc - 1);
+    const int k0 = t * KEYS;
+    const uint16_t* Ks = smem + sc * STAGE;
+    const uint16_t* Vs = Ks + TILE;
+    bool full = k0 + KEYS <= a.Lkv;
+    if (a.causal) full = full && (k0 + KEYS - 1 <= pos_min);
+    if (a.window > 0) {
+      full = full && (pos_max - k0 < a.window);
+      if (!a.causal) full = full && (k0 + KEYS - 1 - pos_min < a.window);
+    }
+    tile_pair<T, DQK, DV, NQB, 0, 0, true, SOFTCAP, MGQA_EARLY_FRAG>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16, g4);
+    sc = (sc == 2) ? 0 : sc + 1;
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float l = l_p[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, D, g4);
   }
 }
 
@@ -902,7 +1168,10 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   if (plan.path == kPathDecode) {
     hipLaunchKernelGGL((decode_kernel<T, DQK, DV, SOFTCAP>), grid, block, 0, st, args);
   } else if (plan.nwaves == 8 && plan.nqb == 2) {
-    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
+    if (args.d == 128)
+      hipLaunchKernelGGL((prefill128_kernel<T, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
+    else
+      hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 1, 4, SOFTCAP>), grid, block, 0, st, args);
   }

@@ -59,3 +59,45 @@ def test_workload_parity(name):
     print(name, st, flush=True)
     assert ok, f"{name}: {st}"
     assert st["nrmse"] < 1e-2, f"{name}: {st}"
+
+
+# Shapes large enough (>= 512 workgroups) that the plan picks the 8-wave,
+# 256-row prefill blocks -- for head size 128 the variant that fills LDS with
+# direct global-to-LDS loads -- checked on sampled rows.
+LARGE_BLOCK_CASES = [
+    # name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed
+    ("lb_causal_window_cap_d128", 2, 32, 16, 2048, 2048, 128, True, 300, 20.0, "bf16", 201),
+    ("lb_bottom_right_ragged_d128", 2, 32, 16, 2100, 2213, 128, True, 0, 0.0, "bf16", 202),
+    ("lb_noncausal_window_d128", 2, 32, 16, 2048, 2048, 128, False, 200, 0.0, "bf16", 203),
+    ("lb_fp16_d128", 2, 32, 16, 2048, 2048, 128, True, 0, 0.0, "fp16", 204),
+    ("lb_causal_d64", 2, 32, 16, 2048, 2048, 64, True, 0, 0.0, "bf16", 205),
+    ("lb_window_cap_d96_g8", 4, 64, 8, 1024, 1100, 96, True, 129, 30.0, "bf16", 206),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_BLOCK_CASES, ids=lambda c: c[0])
+def test_large_block_parity(case):
+    from masked_gqa_attention_amd import _lib
+    name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed = case
+    rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), window, softcap,
+                              0 if dtype == "bf16" else 1)
+    assert rc == 0 and plan["path"] == 0 and plan["rows_per_wg"] == 256, plan
+    announce(f"large block {name}")
+    q = synth.draw_array(seed, (B, Hq, Lq, d), dtype)
+    k = synth.draw_array(seed + 1, (B, Hkv, Lkv, d), dtype)
+    v = synth.draw_array(seed + 2, (B, Hkv, Lkv, d), dtype)
+    if softcap > 0:  # hot queries so the softcap matters
+        q = synth.f32_to_storage((synth.storage_to_f64(q, dtype) * 4).astype(np.float32), dtype)
+    got = run(q, k, v, dtype, causal, window, softcap)
+    qf = synth.storage_to_f64(q, dtype)
+    kf = synth.storage_to_f64(k, dtype)
+    vf = synth.storage_to_f64(v, dtype)
+    w = synth.Workload(name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap)
+    rows = _sample_rows(w.with_(window=max(window, 64)), n_random=160, seed=seed)
+    ref = oracle.attention_rows(qf, kf, vf, rows, causal, window, softcap)
+    sel = np.stack([got[b, h, i] for (b, h, i) in rows])
+    ok, st = compare(sel, ref)
+    assert np.isfinite(got).all()
+    print(name, st, flush=True)
+    assert ok, f"{name}: {st}"
+    assert st["nrmse"] < 1e-2, f"{name}: {st}"
