@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kCUs = 256;              // MI355X compute units
 #ifndef MGQA_DECODE_TARGET_WGS
-#define MGQA_DECODE_TARGET_WGS 512
+#define MGQA_DECODE_TARGET_WGS 256
 #endif
 // Prefill block shape (waves per workgroup, 16-row blocks per wave); the
 // kernels are instantiated for 4x1 and 8x2.
@@ -25,7 +25,7 @@ constexpr int kCUs = 256;              // MI355X compute units
 #ifndef MGQA_PREFILL_NQB
 #define MGQA_PREFILL_NQB 2
 #endif
-// Decode: split the key band until about this many workgroups run (two per CU).
+// Decode: split the key band until about this many workgroups run (one per CU).
 constexpr long long kTargetWGs = MGQA_DECODE_TARGET_WGS;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

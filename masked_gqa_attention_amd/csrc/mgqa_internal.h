@@ -9,7 +9,11 @@ namespace mgqa {
 
 // Keys per staged tile.
 constexpr int kPrefillKeys = 64;   // prefill/encoder: every wave sweeps the whole tile
-constexpr int kDecodeKeys = 128;   // split decode: each of the 4 waves takes 32 keys
+#ifndef MGQA_DECODE_WAVES
+#define MGQA_DECODE_WAVES 8
+#endif
+constexpr int kDecodeWaves = MGQA_DECODE_WAVES;  // split decode: waves per workgroup
+constexpr int kDecodeKeys = 32 * kDecodeWaves;    // each wave takes 32 keys of a tile
 constexpr int kThreads = 256;      // 4 wave64 per workgroup
 constexpr int kMaxRowsDecode = 16; // one 16-column MFMA block of (head, position) rows
 

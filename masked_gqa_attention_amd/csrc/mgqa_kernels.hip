@@ -14,18 +14,20 @@
 //     row is a (query head of the group, query position) pair, so one K/V tile
 //     staged in LDS feeds all G query heads that share the kv head.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32:
-//     the accumulator layout of S^T (lane = query column, 4 consecutive key
-//     rows per lane group) is exactly the B-operand layout P^T needs for the
-//     second product O^T = V^T P^T, so probabilities never leave registers.
-//     The key order inside a 32-key step is permuted so each lane group holds
-//     8 consecutive keys, which makes the V^T operand one 16-byte LDS read.
-//   * K is staged row-major, V is staged transposed (V^T) in LDS; rows are
-//     padded by 16 bytes.
+//     the accumulator layout of S^T (lane = query column, 4 consecutive keys
+//     per lane group and 16-key block) is the B-operand layout P^T needs for
+//     the second product O^T = V^T P^T, so probabilities never leave
+//     registers.  The V^T operand comes from row-major V in LDS through the
+//     transposing LDS read ds_read_b64_tr_b16.
+//   * K and V tiles are staged row-major: through registers with buffer loads
+//     (padded rows), or -- head size 128 -- straight from HBM into LDS with
+//     buffer loads that write LDS (dense rows, swizzled 16-byte slots).  Keys
+//     past the end fall outside the buffer range and read as zero.
 //   * Tiles wholly outside the causal/window band are never visited; tiles
 //     wholly inside skip the mask arithmetic.
 //   * Online softmax in base 2 with a lazily updated reference maximum: the
 //     accumulators are rescaled only when a row maximum grows by more than
-//     2^8, so probabilities stay below 256 and most tiles skip the rescale.
+//     2^8, so probabilities stay below 256 and most steps skip the rescale.
 //   * Decode (G*Lq <= 16 rows per kv head) splits the key band over
 //     workgroups; each writes fp32 partials (max, sum, unnormalised output) and
 //     the last workgroup to arrive for a (batch, kv head) combines all splits in
@@ -139,220 +141,6 @@ __device__ __forceinline__ bool key_visible(int j, int pos, int Lkv, int causal,
   return ok;
 }
 
-// Maximum raw score -> base-2 exponent units (monotone map).
-template <bool SOFTCAP>
-__device__ __forceinline__ float max_to_exp_units(float mx, const KernelArgs& a) {
-  if (mx == kNegInf) return kNegInf;
-  if (SOFTCAP) return a.c2 * tanhf(mx * a.beta);
-  return mx * a.alpha;
-}
-
-// ---------------------------------------------------------------------------
-// LDS staging.  K: [keys][DQK*32 + 8] row-major.  V^T: [DV*16][keys + 8].
-// Keys past Lkv and head-size columns past d are zero-filled, so padded
-// columns contribute exactly 0 to both products.
-// ---------------------------------------------------------------------------
-//
-// A tile is moved in two phases so that every global load of a tile is in
-// flight at once and the next tile's loads overlap the current tile's math:
-// load() issues unconditional 16-byte loads into registers (an out-of-range
-// element reads the unit's first row instead and is then replaced by zero),
-// store() writes the registers to LDS.
-template <int KEYS, int DQK>
-struct KTile {
-  static constexpr int KP = DQK * 32 + 8;
-  static constexpr int CH = DQK * 4;  // 8-element chunks per padded row
-  static constexpr int TOTAL = KEYS * CH;
-  static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
-  u32x4 r[PER];
-  uint32_t okmask;  // bit it: element `it` is inside the tensor (zero-filled otherwise)
-
-  __device__ __forceinline__ void load(const uint16_t* kg, int k0, int Lkv, int d, int tid) {
-    okmask = 0u;
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int c = tid + it * kThreads;
-      const int key = c / CH, ch = c % CH;
-      const bool ok = (TOTAL % kThreads == 0 || c < TOTAL) && (k0 + key < Lkv) && (ch * 8 < d);
-      r[it] = ldg16(ok ? kg + (size_t)(k0 + key) * d + ch * 8 : kg);
-      okmask |= ok ? (1u << it) : 0u;
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* Ks, int tid) const {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int c = tid + it * kThreads;
-      if (TOTAL % kThreads == 0 || c < TOTAL)
-        *reinterpret_cast<u32x4*>(Ks + (c / CH) * KP + (c % CH) * 8) =
-            ((okmask >> it) & 1u) ? r[it] : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-};
-
-// Each thread moves 4 consecutive keys x 8 head-size columns and writes them
-// transposed: 8 LDS rows of V^T, 4 keys (8 bytes) each.
-template <int KEYS, int DV>
-struct VtTile {
-  static constexpr int VP = KEYS + 8;
-  static constexpr int KG = KEYS / 4;  // 4-key groups
-  static constexpr int DC = DV * 2;    // 8-column chunks of the padded head size
-  static constexpr int TOTAL = KG * DC;
-  static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
-  u32x4 r[PER][4];
-  uint32_t okmask;  // bit 4*it + rr: element inside the tensor (zero-filled otherwise)
-
-  __device__ __forceinline__ void load(const uint16_t* vg, int k0, int Lkv, int d, int tid) {
-    okmask = 0u;
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int c = tid + it * kThreads;
-      const int kgi = c % KG, dc = c / KG;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + kgi * 4 + rr;
-        const bool ok = (TOTAL % kThreads == 0 || c < TOTAL) && (key < Lkv) && (dc * 8 < d);
-        r[it][rr] = ldg16(ok ? vg + (size_t)key * d + dc * 8 : vg);
-        okmask |= ok ? (1u << (4 * it + rr)) : 0u;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* Vt, int tid) const {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int c = tid + it * kThreads;
-      if (TOTAL % kThreads == 0 || c < TOTAL) {
-        const int kgi = c % KG, dc = c / KG;
-        u16x8 rows[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          rows[rr] = __builtin_bit_cast(
-              u16x8, ((okmask >> (4 * it + rr)) & 1u) ? r[it][rr] : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          u16x4 col = {rows[0][i], rows[1][i], rows[2][i], rows[3][i]};
-          *reinterpret_cast<u16x4*>(Vt + (dc * 8 + i) * VP + kgi * 4) = col;
-        }
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// One wave, NQB query blocks of 16 rows, NK32 steps of 32 keys starting at
-// tile-local key `kbase`.  Updates the online-softmax state in place.
-//
-// S^T block (step tt, half hh) row rho holds tile-local key
-//   kbase + 32*tt + 8*(rho/4) + 4*hh + rho%4,
-// so after the MFMA lane group g4 holds keys kbase + 32*tt + 8*g4 + [0..7]
-// across the two halves: the P^T operand of step tt, in key order.
-// ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NQB, int NK32, int KEYS, bool SOFTCAP>
-__device__ __forceinline__ void wave_step(const uint16_t* Ks, const uint16_t* Vt, int kbase,
-                                          int kglob0, bool full, const u32x4 (&qf)[NQB][DQK],
-                                          const int (&qpos)[NQB], float (&m_e)[NQB],
-                                          float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
-                                          const KernelArgs& a, int lane) {
-  constexpr int KP = DQK * 32 + 8;
-  constexpr int VP = KEYS + 8;
-  const int c16 = lane & 15, g4 = lane >> 4;
-
-  // ---- S^T = K Q^T -------------------------------------------------------
-  f32x4 s[NQB][NK32][2];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int tt = 0; tt < NK32; ++tt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) s[qb][tt][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int tt = 0; tt < NK32; ++tt) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int krow = kbase + 32 * tt + 8 * (c16 >> 2) + 4 * hh + (c16 & 3);
-#pragma unroll
-      for (int t = 0; t < DQK; ++t) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + krow * KP + 32 * t + 8 * g4);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][tt][hh] = Elem<T>::mfma(kf, qf[qb][t], s[qb][tt][hh]);
-      }
-    }
-  }
-
-  // ---- mask, online softmax, probabilities ---------------------------------
-  u32x4 pk[NQB][NK32];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    if (!full) {
-#pragma unroll
-      for (int tt = 0; tt < NK32; ++tt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = kglob0 + kbase + 32 * tt + 8 * g4 + 4 * hh + i;
-            if (!key_visible(j, qpos[qb], a.Lkv, a.causal, a.window)) s[qb][tt][hh][i] = kNegInf;
-          }
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int tt = 0; tt < NK32; ++tt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][tt][hh][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxe = max_to_exp_units<SOFTCAP>(mx, a);
-    if (mxe > m_e[qb] + kRescaleSlack) {
-      const float f = fast_exp2(m_e[qb] - mxe);  // 0 when m_e was -inf
-      m_e[qb] = mxe;
-      l_p[qb] *= f;
-#pragma unroll
-      for (int db = 0; db < DV; ++db) o[qb][db] *= f;
-    }
-    const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
-    float lsum = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < NK32; ++tt) {
-      float p[8];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = s[qb][tt][hh][i];
-          float pv;
-          if (SOFTCAP) {
-            // c*tanh(u) = c - 2c/(exp(2u)+1); in base-2 units the exponent is
-            // c2 - 2*c2*r - mref with r = 1/(2^(x*gamma) + 1).
-            const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
-            pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
-            if (!full && x == kNegInf) pv = 0.f;
-          } else {
-            pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
-          }
-          p[hh * 4 + i] = pv;
-          lsum += pv;
-        }
-      pk[qb][tt] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
-                         Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
-    }
-    l_p[qb] += lsum;
-  }
-
-  // ---- O^T += V^T P^T ----------------------------------------------------------
-#pragma unroll
-  for (int tt = 0; tt < NK32; ++tt) {
-#pragma unroll
-    for (int db = 0; db < DV; ++db) {
-      const u32x4 vf =
-          *reinterpret_cast<const u32x4*>(Vt + (db * 16 + c16) * VP + kbase + 32 * tt + 8 * g4);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[qb][tt], o[qb][db]);
-    }
-  }
-}
-
 // Load this lane's Q^T operand (16 query columns, 8 head-size elements per
 // lane group and 32-wide step).  Rows outside the problem load zeros.
 template <int DQK>
@@ -401,24 +189,32 @@ template <int KEYS, int CH, int PITCH, int NT>
 struct RowTile {
   static constexpr int TOTAL = KEYS * CH;
   static constexpr int PER = (TOTAL + NT - 1) / NT;
+  // When NT is a multiple of CH every load of a thread has the same column
+  // chunk, so one base offset and a uniform row step describe all of them.
+  static constexpr bool COMPACT = (NT % CH == 0) && (TOTAL % NT == 0);
+  static constexpr int NOFF = COMPACT ? 1 : PER;
   u32x4 r[PER];
-  int voff[PER];
+  int voff[NOFF];
+  int vstep;  // bytes between consecutive loads of a thread (COMPACT only)
 
   __device__ __forceinline__ void init(int d, int tid) {
+    vstep = (NT / CH) * d * 2;
 #pragma unroll
-    for (int it = 0; it < PER; ++it) {
+    for (int it = 0; it < NOFF; ++it) {
       const int c = tid + it * NT;
       const int key = c / CH, ch = c % CH;
       const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (ch * 8 < d);
-      voff[it] = ok ? (key * d + ch * 8) * 2 : 0x7FFFFFF0;
+      voff[it] = ok ? (key * d + ch * 8) * 2 : 0x7FFF0000;
     }
   }
   // g: the (batch, kv head) unit's first row; loads keys k0 .. k0+KEYS-1.
   __device__ __forceinline__ void load(const uint16_t* g, int k0, int Lkv, int d) {
     const auto rs = make_rsrc(g + (size_t)k0 * d, (uint32_t)(Lkv - k0) * (uint32_t)d * 2u);
 #pragma unroll
-    for (int it = 0; it < PER; ++it)
-      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[it], 0, 0));
+    for (int it = 0; it < PER; ++it) {
+      const int vo = COMPACT ? voff[0] + it * vstep : voff[it];
+      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+    }
   }
   __device__ __forceinline__ void store(uint16_t* sm, int tid) const {
 #pragma unroll
@@ -938,28 +734,30 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV decode kernel: one workgroup per (unit = batch*Hkv + kv head,
-// split).  The 16 rows are (head of the group, position) pairs, head fastest,
-// nrows = G*Lq <= 16 of them real.  Each 128-key tile is staged once; wave w
-// takes keys [32w, 32w+32).  The four wave states are merged in LDS, then the
-// split's partial is written, and the last split to arrive for the unit merges
-// all partials in split order and writes the output.
+// Split-KV decode kernel: one workgroup of NW waves per (unit = batch*Hkv +
+// kv head, split).  The 16 rows are (head of the group, position) pairs, head
+// fastest, nrows = G*Lq <= 16 of them real.  Each 32*NW-key tile is staged
+// once (K and V row-major, V read transposed); wave w takes keys
+// [32w, 32w+32) of it.  The wave states are merged in LDS, then the split's
+// partial is written, and the last split to arrive for the unit merges all
+// partials in split order and writes the output.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
-  constexpr int KEYS = kDecodeKeys;
+template <typename T, int DQK, int DV, int NW, bool SOFTCAP>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int KEYS = 32 * NW;
   constexpr int KP = DQK * 32 + 8;
-  constexpr int VP = KEYS + 8;
+  constexpr int VP = DV * 16 + 16;
   constexpr int DVP = DV * 16;
   constexpr int OP = DVP + 4;  // LDS pitch of the merged wave outputs (floats)
-  // K and V^T tiles; after the key loop the same bytes hold the wave outputs.
-  constexpr int TILE_BYTES = (KEYS * KP + DVP * VP) * 2;
-  constexpr int MERGE_BYTES = 4 * 16 * OP * 4;
+  // K and V tiles; after the key loop the same bytes hold the wave outputs.
+  constexpr int TILE_BYTES = KEYS * (KP + VP) * 2;
+  constexpr int MERGE_BYTES = NW * 16 * OP * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vt = Ks + KEYS * KP;
+  uint16_t* Vs = Ks + KEYS * KP;
   float (*wo)[16 * OP] = reinterpret_cast<float (*)[16 * OP]>(smem);
-  __shared__ float wm[4][16], wl[4][16];
+  __shared__ float wm[NW][16], wl[NW][16];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -974,6 +772,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * d;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * d;
   uint16_t* og = static_cast<uint16_t*>(a.out);
+
+  const int pos_min = off, pos_max = off + a.Lq - 1;
+  const int t0 = a.t_begin + split * a.tiles_per_split;
+  const int t1 = min(a.t_end, t0 + a.tiles_per_split);
+  RowTile<KEYS, DQK * 4, KP, NT> kt;
+  RowTile<KEYS, DV * 2, VP, NT> vt;
+  kt.init(d, tid);
+  vt.init(d, tid);
+  if (t0 < t1) {
+    kt.load(kg, t0 * KEYS, a.Lkv, d);
+    vt.load(vg, t0 * KEYS, a.Lkv, d);
+  }
 
   // This lane's row (column c16 of the single query block).
   const int r = c16;
@@ -990,25 +800,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
 #pragma unroll
   for (int db = 0; db < DV; ++db) o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int pos_min = off, pos_max = off + a.Lq - 1;
-  const int t0 = a.t_begin + split * a.tiles_per_split;
-  const int t1 = min(a.t_end, t0 + a.tiles_per_split);
-  KTile<KEYS, DQK> kt;
-  VtTile<KEYS, DV> vt;
-  if (t0 < t1) {
-    kt.load(kg, t0 * KEYS, a.Lkv, d, tid);
-    vt.load(vg, t0 * KEYS, a.Lkv, d, tid);
-  }
+  u32x4 kf_unused[2][DQK];
   for (int t = t0; t < t1; ++t) {
     const int k0 = t * KEYS;
-    __syncthreads();
+    __syncthreads();  // every wave is done with the previous tile
     kt.store(Ks, tid);
-    vt.store(Vt, tid);
-    __syncthreads();
-    if (t + 1 < t1) {
-      kt.load(kg, k0 + KEYS, a.Lkv, d, tid);
-      vt.load(vg, k0 + KEYS, a.Lkv, d, tid);
+    vt.store(Vs, tid);
+    if (t + 1 < t1) {  // registers are free again: next tile's loads fly during this one
+      kt.load(kg, k0 + KEYS, a.Lkv, d);
+      vt.load(vg, k0 + KEYS, a.Lkv, d);
     }
+    __syncthreads();
     // Full-tile test on this wave's 32 keys.
     const int w0 = k0 + 32 * wave;
     bool full = w0 + 32 <= a.Lkv;
@@ -1017,11 +819,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
       full = full && (pos_max - w0 < a.window);
       if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
     }
-    wave_step<T, DQK, DV, 1, 1, KEYS, SOFTCAP>(Ks, Vt, 32 * wave, k0, full, qf, qpos, m_e, l_p, o,
-                                               a, lane);
+    if (full)
+      tile_step<T, DQK, DV, 1, KP, VP, false, SOFTCAP, false, false, false>(
+          Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
+    else
+      tile_step<T, DQK, DV, 1, KP, VP, false, SOFTCAP, true, false, false>(
+          Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
   }
 
-  // ---- merge the four wave states (fixed order) -----------------------------
+  // ---- merge the wave states (fixed order) ------------------------------------
   __syncthreads();  // every wave is done reading the tiles that wo overwrites
   float l = l_p[0];
   l += __shfl_xor(l, 16);
@@ -1036,25 +842,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
     for (int i = 0; i < 4; ++i) wo[wave][c16 * OP + 16 * db + 4 * g4 + i] = o[0][db][i];
   __syncthreads();
 
-  // Thread -> float4 chunks q = tid + 256*j of the [nrows][DVP] output block:
+  // Thread -> float4 chunks q = tid + NT*j of the [nrows][DVP] output block:
   // row q / CPR, columns 4*(q % CPR) .. +3, so a wave touches contiguous memory.
   constexpr int CPR = DVP / 4;
-  constexpr int JN = (16 * CPR + kThreads - 1) / kThreads;
+  constexpr int JN = (16 * CPR + NT - 1) / NT;
   const int nch = a.nrows * CPR;
   float M[JN], L[JN];
   f32x4 acc[JN];
 #pragma unroll
   for (int j = 0; j < JN; ++j) {
-    const int q = tid + j * kThreads;
+    const int q = tid + j * NT;
     const int row = min(q / CPR, 15), c4 = q % CPR;
     M[j] = kNegInf;
     L[j] = 0.f;
     acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M[j] = fmaxf(M[j], wm[w][row]);
+    for (int w = 0; w < NW; ++w) M[j] = fmaxf(M[j], wm[w][row]);
     if (M[j] != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2(wm[w][row] - M[j]);
         L[j] += f * wl[w][row];
         const f32x4 x = *reinterpret_cast<const f32x4*>(&wo[w][row * OP + 4 * c4]);
@@ -1066,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
   if (a.nsplit == 1) {
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
-      const int q = tid + j * kThreads;
+      const int q = tid + j * NT;
       const int row = q / CPR, c4 = q % CPR;
       if (q < nch && 4 * c4 < d) {
         const float inv = 1.0f / L[j];
@@ -1086,7 +892,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
   const int pidx = (unit * a.nsplit + split) * a.nrows;
 #pragma unroll
   for (int j = 0; j < JN; ++j) {
-    const int q = tid + j * kThreads;
+    const int q = tid + j * NT;
     const int row = q / CPR, c4 = q % CPR;
     if (q < nch) {
       st_dev16(rs_o, ((pidx + row) * DVP + 4 * c4) * 4, acc[j]);
@@ -1104,13 +910,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
   if (!last_flag) return;
 
   // ---- last arrival: merge all splits in split order ---------------------------------
-  // Online merge over groups of 8 splits; every load of a group is issued
+  // Online merge over groups of 16 splits; every load of a group is issued
   // before any of them is used.
-  constexpr int CHUNK = 8;
+  constexpr int CHUNK = 16;
   const int base = unit * a.nsplit * a.nrows;
 #pragma unroll
   for (int j = 0; j < JN; ++j) {
-    const int q = tid + j * kThreads;
+    const int q = tid + j * NT;
     if (q >= nch) continue;
     const int row = q / CPR, c4 = q % CPR;
     float Mg = kNegInf, Lg = 0.f;
@@ -1166,7 +972,8 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   const dim3 block(kThreads);
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathDecode) {
-    hipLaunchKernelGGL((decode_kernel<T, DQK, DV, SOFTCAP>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((decode_kernel<T, DQK, DV, kDecodeWaves, SOFTCAP>), grid, dim3(64 * kDecodeWaves), 0,
+                       st, args);
   } else if (plan.nwaves == 8 && plan.nqb == 2) {
     if (args.d == 128)
       hipLaunchKernelGGL((prefill128_kernel<T, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
