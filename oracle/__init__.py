@@ -19,3 +19,4 @@ from .attention_fp64 import (  # noqa: F401
     visible_pairs,
 )
 from .brute import attention_brute  # noqa: F401
+from .kvcache import kv_cache_update  # noqa: F401
