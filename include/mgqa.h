@@ -61,9 +61,11 @@ extern "C" {
 #define MGQA_ERR_HIP       -8  /* a HIP runtime call or kernel launch failed          */
 #define MGQA_ERR_DTYPE     -9  /* dtype not MGQA_BF16 / MGQA_FP16                      */
 #define MGQA_ERR_RANGE    -10  /* a size too large for the library's 32-bit indexing  */
+#define MGQA_ERR_UNSUPPORTED -11 /* a valid combination this library does not run      */
 
 #define MGQA_BF16 0
 #define MGQA_FP16 1
+#define MGQA_F32  2  /* KV-cache storage only (kv_cache_append) */
 
 /* Masked GQA attention forward, bf16 in and out.  window <= 0 means no window,
  * softcap <= 0 means no softcap, causal is 0 or 1.  Allocates its own
@@ -89,6 +91,38 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                 int B, int Hq, int Hkv, int Lq, int Lkv, int d,
                 int causal, int window, float softcap, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention over the first `length` keys of a KV cache of S slots per
+ * (batch, kv head): K/V rows of head (b, g) start at element (b*Hkv + g)*S*d
+ * ([B][Hkv][S][d], the layout kv_cache_append writes with layout 1).  Same
+ * operation, options, dtypes, workspace rules and errors as attn_fwd_ex with
+ * Lkv = length (attn_workspace_bytes with Lkv = length gives the workspace).
+ *
+ * ring_start = -1: keys 0..length-1 are slots 0..length-1.
+ * ring_start in [0, S): ring buffer; logical key j (0 <= j < length <= S) is
+ * slot (ring_start + j) mod S, and the causal/window rules apply to logical
+ * positions.  A sliding-window decode over a ring of S = W slots is the same
+ * attention as a linear decode over the last W keys (the "ring or linear
+ * windows" of the Metal attention pull request).  The ring form runs on the
+ * decode path only (Hq/Hkv * Lq <= 16); otherwise MGQA_ERR_UNSUPPORTED. */
+int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void* out,
+                   int B, int Hq, int Hkv, int Lq, int S, int length, int ring_start, int d,
+                   int causal, int window, float softcap, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* KV-cache update at a position (TensorTonic, "KV Cache Update at a
+ * Position"): for every batch row and head, slots position .. position+L-1 of
+ * k_cache / v_cache receive the L new float32 vectors converted to the cache
+ * type (round to nearest even); every other slot is left untouched.
+ *   layout 0: caches [B][S][H][D], new vectors [B][L][H][D] (the page's layout)
+ *   layout 1: caches [B][H][S][D], new vectors [B][H][L][D] (attn_fwd_cache's)
+ * cache_dtype: MGQA_F32, MGQA_BF16 or MGQA_FP16.  Requires 0 <= position <= S-L
+ * (else MGQA_ERR_RANGE).  If length_out (device int32) is not NULL, the kernel
+ * writes position + L there.  Caches are updated in place on `stream`; new_k,
+ * new_v must not overlap the caches.  D may be any positive size. */
+int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const float* new_v,
+                    int B, int S, int H, int D, int L, int position, int cache_dtype, int layout,
+                    int* length_out, void* stream);
 
 /* Plan the library would use for this shape, without touching the GPU.
  * info[0] path (0 = prefill/encoder kernel, 1 = split-KV decode kernel)

@@ -8,11 +8,12 @@ call does, and raises if it was not built.
 """
 from .synth import WORKLOADS, Workload  # noqa: F401
 
-__all__ = ["attn", "attn_fwd", "make_attention", "WORKLOADS", "Workload"]
+__all__ = ["attn", "attn_fwd", "attn_cache", "kv_cache_append", "make_attention", "WORKLOADS",
+           "Workload"]
 
 
 def __getattr__(name):
-    if name in ("attn", "attn_fwd", "make_attention", "MgqaError"):
+    if name in ("attn", "attn_fwd", "attn_cache", "kv_cache_append", "make_attention", "MgqaError"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

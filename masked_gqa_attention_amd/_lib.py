@@ -26,13 +26,15 @@ MGQA_ERR_WORKSPACE = -7
 MGQA_ERR_HIP = -8
 MGQA_ERR_DTYPE = -9
 MGQA_ERR_RANGE = -10
+MGQA_ERR_UNSUPPORTED = -11
 
 MGQA_BF16 = 0
 MGQA_FP16 = 1
+MGQA_F32 = 2
 
 # Every symbol the header declares.
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_workspace_bytes", "attn_plan",
-           "attn_error_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_cache", "kv_cache_append", "attn_workspace_bytes",
+           "attn_plan", "attn_error_string", "attn_version")
 
 _lib = None
 
@@ -55,6 +57,10 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd.restype = i
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_fwd_ex.restype = i
+    lib.attn_fwd_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_fwd_cache.restype = i
+    lib.kv_cache_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp]
+    lib.kv_cache_append.restype = i
     lib.attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     lib.attn_workspace_bytes.restype = sz
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, i, f, i, ctypes.POINTER(ctypes.c_longlong)]
@@ -80,6 +86,19 @@ def attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, d
                 workspace, workspace_bytes, stream) -> int:
     return load().attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window),
                               float(softcap), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, length, ring_start, d, causal,
+                   window, softcap, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, length, ring_start, d,
+                                 int(causal), int(window), float(softcap), int(dtype), workspace,
+                                 int(workspace_bytes), stream)
+
+
+def kv_cache_append(k_cache, v_cache, new_k, new_v, B, S, H, D, L, position, cache_dtype, layout,
+                    length_out, stream) -> int:
+    return load().kv_cache_append(k_cache, v_cache, new_k, new_v, B, S, H, D, L, position,
+                                  int(cache_dtype), int(layout), length_out, stream)
 
 
 def attn_workspace_bytes(B, Hq, Hkv, Lq, Lkv, d, causal, window) -> int:

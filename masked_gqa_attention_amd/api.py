@@ -94,6 +94,78 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         raise MgqaError(rc, "attn_fwd")
 
 
+_CACHE_DTYPES = {torch.bfloat16: _lib.MGQA_BF16, torch.float16: _lib.MGQA_FP16,
+                 torch.float32: _lib.MGQA_F32}
+
+
+def kv_cache_append(k_cache: torch.Tensor, v_cache: torch.Tensor, new_k: torch.Tensor,
+                    new_v: torch.Tensor, position: int, layout: int = 1,
+                    length_out: torch.Tensor | None = None) -> int:
+    """Write L new float32 key/value vectors into the caches at `position`
+    (in place) and return position + L.  layout 1: caches [B,H,S,D], new
+    [B,H,L,D] (what attn_cache reads); layout 0: caches [B,S,H,D], new
+    [B,L,H,D].  If length_out (int32 device scalar) is given, the kernel writes
+    position + L into it as well."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("new_k", new_k), ("new_v", new_v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if k_cache.dtype not in _CACHE_DTYPES or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must share one dtype: float32, bfloat16 or float16")
+    if new_k.dtype != torch.float32 or new_v.dtype != torch.float32:
+        raise ValueError("new vectors must be float32")
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or new_k.shape != new_v.shape:
+        raise ValueError("caches and new vectors must be 4-D, pairwise of one shape")
+    if layout == 1:
+        B, H, S, D = k_cache.shape
+        L = new_k.shape[2]
+        ok = new_k.shape == (B, H, L, D)
+    else:
+        B, S, H, D = k_cache.shape
+        L = new_k.shape[1]
+        ok = new_k.shape == (B, L, H, D)
+    if not ok:
+        raise ValueError("new vectors do not match the cache shape for this layout")
+    if length_out is not None and (length_out.dtype != torch.int32 or not length_out.is_cuda):
+        raise ValueError("length_out must be an int32 GPU tensor")
+    stream = torch.cuda.current_stream(k_cache.device).cuda_stream
+    rc = _lib.kv_cache_append(k_cache.data_ptr(), v_cache.data_ptr(), new_k.data_ptr(),
+                              new_v.data_ptr(), B, S, H, D, L, position, _CACHE_DTYPES[k_cache.dtype],
+                              layout, length_out.data_ptr() if length_out is not None else None,
+                              stream)
+    if rc != 0:
+        raise MgqaError(rc, "kv_cache_append")
+    return position + L
+
+
+def attn_cache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, length: int,
+               causal: bool = False, window: int = 0, softcap: float = 0.0, ring_start: int = -1,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Attention of q [B,Hq,Lq,d] over the first `length` keys of caches
+    [B,Hkv,S,d] (ring_start = -1), or over a ring buffer whose logical key j is
+    slot (ring_start + j) % S."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype, bfloat16 or float16")
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, S, dk = k_cache.shape
+    if Bk != B or dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    nbytes = _lib.attn_workspace_bytes(B, Hq, Hkv, Lq, length, d, causal, window)
+    ws = _workspace(nbytes, q.device, stream)
+    rc = _lib.attn_fwd_cache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                             B, Hq, Hkv, Lq, S, length, ring_start, d, causal, window, softcap,
+                             _DTYPES[q.dtype], ws.data_ptr() if ws is not None else None, nbytes,
+                             stream)
+    if rc != 0:
+        raise MgqaError(rc, "attn_fwd_cache")
+    return out
+
+
 def make_attention(cfg: dict):
     """cfg keys: batch, q_len, kv_len, num_q_heads, num_kv_heads, head_dim,
     causal, window, softcap (seed and name are accepted and ignored: the

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmgqa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["mgqa_api.cpp", "mgqa_kernels.hip"]
+SOURCES = ["mgqa_api.cpp", "mgqa_kernels.hip", "mgqa_cache.hip"]
 
 ARCH = "gfx950"
 COMMON = [

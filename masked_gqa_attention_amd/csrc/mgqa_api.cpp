@@ -128,6 +128,9 @@ static KernelArgs make_args(const Plan& p, const void* q, const void* k, const v
   a.Lq = Lq;
   a.Lkv = Lkv;
   a.d = d;
+  a.kv_stride = (long long)Lkv * d;
+  a.ring_start = -1;
+  a.ring_slots = Lkv;
   a.causal = causal;
   a.window = window;
   const double log2e = 1.4426950408889634;
@@ -182,7 +185,8 @@ const char* attn_error_string(int code) {
     case MGQA_ERR_WORKSPACE: return "workspace missing or smaller than attn_workspace_bytes()";
     case MGQA_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case MGQA_ERR_DTYPE: return "dtype must be MGQA_BF16 (0) or MGQA_FP16 (1)";
-    case MGQA_ERR_RANGE: return "a size exceeds the library's indexing range";
+    case MGQA_ERR_RANGE: return "a size or position out of range (indexing limit, cache length, ring start, append position)";
+    case MGQA_ERR_UNSUPPORTED: return "unsupported combination: a ring-buffer cache needs the decode path (Hq/Hkv * Lq <= 16)";
     default: return "unknown error code";
   }
 }
@@ -224,6 +228,49 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
   const KernelArgs a = make_args(p, q, k, v, out, Hq, Hkv, Lq, Lkv, d, causal, window, softcap,
                                  p.ws_bytes ? workspace : nullptr);
   if (launch(p, a, dtype, softcap > 0.f, stream) != hipSuccess) return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+
+int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void* out, int B,
+                   int Hq, int Hkv, int Lq, int S, int length, int ring_start, int d, int causal,
+                   int window, float softcap, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!q || !k_cache || !v_cache || !out) return MGQA_ERR_NULL;
+  if (S <= 0 || length <= 0) return MGQA_ERR_SHAPE;
+  if (length > S) return MGQA_ERR_RANGE;
+  if (ring_start < -1 || ring_start >= S) return MGQA_ERR_RANGE;
+  if ((long long)S * d >= (1LL << 31)) return MGQA_ERR_RANGE;
+  Plan p;
+  const int err = make_plan(B, Hq, Hkv, Lq, length, d, causal, window, softcap, dtype, &p);
+  if (err) return err;
+  if (ring_start >= 0 && p.path != kPathDecode) return MGQA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return MGQA_ERR_ALIGN;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return MGQA_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MGQA_ERR_ALIGN;
+  KernelArgs a = make_args(p, q, k_cache, v_cache, out, Hq, Hkv, Lq, length, d, causal, window,
+                           softcap, p.ws_bytes ? workspace : nullptr);
+  a.kv_stride = (long long)S * d;
+  a.ring_start = ring_start;
+  a.ring_slots = S;
+  if (launch(p, a, dtype, softcap > 0.f, stream) != hipSuccess) return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+
+int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const float* new_v, int B,
+                    int S, int H, int D, int L, int position, int cache_dtype, int layout,
+                    int* length_out, void* stream) {
+  if (!k_cache || !v_cache || !new_k || !new_v) return MGQA_ERR_NULL;
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || L <= 0) return MGQA_ERR_SHAPE;
+  if (cache_dtype != MGQA_BF16 && cache_dtype != MGQA_FP16 && cache_dtype != MGQA_F32)
+    return MGQA_ERR_DTYPE;
+  if (layout != 0 && layout != 1) return MGQA_ERR_SHAPE;
+  if (position < 0 || L > S || position > S - L) return MGQA_ERR_RANGE;
+  if ((long long)B * S * H * D >= (1LL << 40) || (long long)B * L * H * D >= (1LL << 31))
+    return MGQA_ERR_RANGE;
+  if (launch_append(k_cache, v_cache, new_k, new_v, B, S, H, D, L, position, cache_dtype, layout,
+                    length_out, stream) != hipSuccess)
+    return MGQA_ERR_HIP;
   return MGQA_OK;
 }
 

@@ -29,6 +29,9 @@ struct KernelArgs {
   float* ws_ml;       // decode partial (max, sum) [unit][split][nrows][2]
   unsigned* ws_cnt;   // decode arrival counters [unit]
   int Hq, Hkv, G, Lq, Lkv, d;
+  long long kv_stride;  // elements between consecutive (batch, kv head) units of K and V
+  int ring_start;       // -1: linear keys; else key j lives in slot (ring_start + j) % ring_slots
+  int ring_slots;
   int causal, window;
   float alpha;        // log2(e)/sqrt(d): raw score -> base-2 exponent units
   float gamma;        // 2*log2(e)/(c*sqrt(d)): softcap exp argument
@@ -69,5 +72,9 @@ int launch(const Plan& plan, const KernelArgs& args, int dtype, bool softcap, vo
 
 // Zero-fills `words` 32-bit words at `p` with a kernel on `stream`.
 int launch_zero(void* p, size_t words, void* stream);
+
+// KV-cache append (arguments validated by the caller).  Returns a hipError_t.
+int launch_append(void* kc, void* vc, const float* nk, const float* nv, int B, int S, int H, int D,
+                  int L, int position, int cache_dtype, int layout, int* length_out, void* stream);
 
 }  // namespace mgqa

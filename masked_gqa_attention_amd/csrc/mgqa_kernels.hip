@@ -216,6 +216,23 @@ struct RowTile {
       r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
     }
   }
+  // Ring-buffer cache: logical key j of the unit lives in slot
+  // (ring_start + j) % S; logical keys at or past Lkv, and chunks past d, read
+  // as zero (offset beyond the unit's range).  g: the unit's slot 0.
+  __device__ __forceinline__ void load_ring(const uint16_t* g, int k0, int Lkv, int d, int ring_start,
+                                            int S, int tid) {
+    const auto rs = make_rsrc(g, (uint32_t)S * (uint32_t)d * 2u);
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + it * NT;
+      const int logical = k0 + c / CH, ch = c % CH;
+      int slot = ring_start + logical;
+      slot -= (slot >= S) ? S : 0;
+      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (logical < Lkv) && (ch * 8 < d);
+      const uint32_t vo = ok ? (uint32_t)(slot * d + ch * 8) * 2u : 0x7FFF0000u;
+      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0));
+    }
+  }
   __device__ __forceinline__ void store(uint16_t* sm, int tid) const {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
@@ -510,8 +527,8 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   const int off = a.Lkv - a.Lq;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * d;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * d;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
   u32x4 qf[NQB][DQK];
@@ -628,8 +645,8 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
   const int off = a.Lkv - a.Lq;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
   // Key band of this block of positions.
@@ -742,7 +759,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
 // partial is written, and the last split to arrive for the unit merges all
 // partials in split order and writes the output.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NW, bool SOFTCAP>
+template <typename T, int DQK, int DV, int NW, bool SOFTCAP, bool RING>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KEYS = 32 * NW;
@@ -769,8 +786,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
   const int off = a.Lkv - a.Lq;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.Lkv * d;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.Lkv * d;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
   const int pos_min = off, pos_max = off + a.Lq - 1;
@@ -780,10 +797,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
   RowTile<KEYS, DV * 2, VP, NT> vt;
   kt.init(d, tid);
   vt.init(d, tid);
-  if (t0 < t1) {
-    kt.load(kg, t0 * KEYS, a.Lkv, d);
-    vt.load(vg, t0 * KEYS, a.Lkv, d);
-  }
+  auto fetch = [&](int k0) {
+    if (RING) {
+      kt.load_ring(kg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
+      vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
+    } else {
+      kt.load(kg, k0, a.Lkv, d);
+      vt.load(vg, k0, a.Lkv, d);
+    }
+  };
+  if (t0 < t1) fetch(t0 * KEYS);
 
   // This lane's row (column c16 of the single query block).
   const int r = c16;
@@ -806,10 +829,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
     __syncthreads();  // every wave is done with the previous tile
     kt.store(Ks, tid);
     vt.store(Vs, tid);
-    if (t + 1 < t1) {  // registers are free again: next tile's loads fly during this one
-      kt.load(kg, k0 + KEYS, a.Lkv, d);
-      vt.load(vg, k0 + KEYS, a.Lkv, d);
-    }
+    if (t + 1 < t1) fetch(k0 + KEYS);  // registers are free again: next tile flies during this one
     __syncthreads();
     // Full-tile test on this wave's 32 keys.
     const int w0 = k0 + 32 * wave;
@@ -972,8 +992,12 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   const dim3 block(kThreads);
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathDecode) {
-    hipLaunchKernelGGL((decode_kernel<T, DQK, DV, kDecodeWaves, SOFTCAP>), grid, dim3(64 * kDecodeWaves), 0,
-                       st, args);
+    if (args.ring_start >= 0)
+      hipLaunchKernelGGL((decode_kernel<T, DQK, DV, kDecodeWaves, SOFTCAP, true>), grid,
+                         dim3(64 * kDecodeWaves), 0, st, args);
+    else
+      hipLaunchKernelGGL((decode_kernel<T, DQK, DV, kDecodeWaves, SOFTCAP, false>), grid,
+                         dim3(64 * kDecodeWaves), 0, st, args);
   } else if (plan.nwaves == 8 && plan.nqb == 2) {
     if (args.d == 128)
       hipLaunchKernelGGL((prefill128_kernel<T, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);

@@ -40,7 +40,7 @@ def test_library_exports_every_header_symbol():
 
 def test_version_and_error_strings():
     assert _lib.attn_version() == 100
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         s = _lib.error_string(code)
         assert s and s != "unknown error code"
     assert _lib.error_string(-99) == "unknown error code"
@@ -88,6 +88,36 @@ def _ex(**kw):
 ])
 def test_validation_codes(kw, code):
     assert _ex(**kw) == code
+
+
+def test_cache_entry_point_validation_codes():
+    f = _lib.attn_fwd_cache
+    args = dict(B=1, Hq=16, Hkv=1, Lq=1, S=4096, length=4096, ring=-1, d=128, causal=1, W=0, cap=0.0,
+                dt=0)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Lq"], a["S"], a["length"], a["ring"],
+                 a["d"], a["causal"], a["W"], a["cap"], a["dt"], None, 0, None)
+    assert call(length=4097) == _lib.MGQA_ERR_RANGE        # length > S
+    assert call(length=0) == _lib.MGQA_ERR_SHAPE
+    assert call(ring=4096) == _lib.MGQA_ERR_RANGE          # ring start outside the cache
+    assert call(ring=-2) == _lib.MGQA_ERR_RANGE
+    assert call(Lq=64, Hq=4, ring=5) == _lib.MGQA_ERR_UNSUPPORTED  # ring needs the decode path
+    assert call() == _lib.MGQA_ERR_WORKSPACE               # split decode without workspace
+    assert f(None, P, P, P, 1, 16, 1, 1, 64, 64, -1, 128, 1, 0, 0.0, 0, None, 0, None) == _lib.MGQA_ERR_NULL
+
+
+def test_append_validation_codes():
+    g = _lib.kv_cache_append
+    assert g(None, P, P, P, 1, 8, 1, 4, 2, 0, 2, 0, None, None) == _lib.MGQA_ERR_NULL
+    assert g(P, P, P, P, 1, 8, 1, 4, 2, 7, 2, 0, None, None) == _lib.MGQA_ERR_RANGE   # pos > S-L
+    assert g(P, P, P, P, 1, 8, 1, 4, 2, -1, 2, 0, None, None) == _lib.MGQA_ERR_RANGE
+    assert g(P, P, P, P, 1, 8, 1, 4, 9, 0, 2, 0, None, None) == _lib.MGQA_ERR_RANGE   # L > S
+    assert g(P, P, P, P, 1, 8, 1, 4, 2, 0, 3, 0, None, None) == _lib.MGQA_ERR_DTYPE
+    assert g(P, P, P, P, 1, 8, 1, 4, 2, 0, 2, 2, None, None) == _lib.MGQA_ERR_SHAPE   # layout
+    assert g(P, P, P, P, 0, 8, 1, 4, 2, 0, 2, 0, None, None) == _lib.MGQA_ERR_SHAPE
 
 
 def test_attn_fwd_validation_codes():
