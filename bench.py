@@ -239,7 +239,7 @@ def main(argv=None) -> int:
         rc, plan = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
                                   w.softcap, 0 if w.dtype == "bf16" else 1)
         results[name] = {"ms": ms, "steps": steps, "copies": copies, **fig,
-                         "kernel": "decode_kernel" if plan.get("path") == 1 else "prefill_kernel",
+                         "kernel": "splitkv_kernel" if plan.get("path") == 1 else "prefill_kernel",
                          "plan": plan, "shape": w.describe()}
         log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
             f"({100 * fig['frac']:.1f}% of {fig['bound']} peak)")

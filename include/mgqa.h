@@ -82,10 +82,11 @@ size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lkv, int d,
 
 /* Same operation with an explicit element type (MGQA_BF16 or MGQA_FP16) and a
  * caller-provided workspace of at least attn_workspace_bytes() bytes (may be
- * NULL when that is 0).  The workspace holds fp32 split partials and per-unit
- * arrival counters.  It must be zero-filled before its first use; every call
- * that completes leaves the counters at zero again, so one workspace can be
- * reused by later calls on the same stream without clearing.  Calls that run
+ * NULL when that is 0).  The workspace holds arrival counters in its first
+ * 1024 bytes (the same bytes for every shape) and fp32 split partials after
+ * them.  It must be zero-filled before its first use; every call that completes
+ * leaves the counters at zero again, so one workspace can be reused by later
+ * calls of any shape on the same stream without clearing.  Calls that run
  * concurrently (different streams) must use different workspaces. */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                 int B, int Hq, int Hkv, int Lq, int Lkv, int d,
@@ -125,10 +126,13 @@ int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const floa
                     int* length_out, void* stream);
 
 /* Plan the library would use for this shape, without touching the GPU.
- * info[0] path (0 = prefill/encoder kernel, 1 = split-KV decode kernel)
+ * info[0] path: 0 = prefill kernel (256-row workgroups, every wave sweeps the
+ *         whole key band), 1 = split-KV kernel (decode, multi-token decode and
+ *         short sequences: the waves of a workgroup, and possibly several
+ *         workgroups, split the key band of its rows)
  * info[1] workgroups launched
  * info[2] query rows (head, position pairs) per workgroup
- * info[3] key splits per (batch, kv-head) unit (1 on the prefill path)
+ * info[3] key splits across workgroups per block of rows (1 on the prefill path)
  * info[4] keys per tile
  * info[5] padded head size used for Q.K^T (multiple of 32)
  * info[6] padded head size used for P.V (multiple of 16)

@@ -14,19 +14,13 @@ namespace mgqa {
 namespace {
 
 constexpr int kCUs = 256;              // MI355X compute units
-#ifndef MGQA_DECODE_TARGET_WGS
-#define MGQA_DECODE_TARGET_WGS 256
+// Split-KV path: position blocks and key splits are chosen so that about this
+// many workgroups run.
+#ifndef MGQA_SPLIT_TARGET_WGS
+#define MGQA_SPLIT_TARGET_WGS 256
 #endif
-// Prefill block shape (waves per workgroup, 16-row blocks per wave); the
-// kernels are instantiated for 4x1 and 8x2.
-#ifndef MGQA_PREFILL_WAVES
-#define MGQA_PREFILL_WAVES 8
-#endif
-#ifndef MGQA_PREFILL_NQB
-#define MGQA_PREFILL_NQB 2
-#endif
-// Decode: split the key band until about this many workgroups run (one per CU).
-constexpr long long kTargetWGs = MGQA_DECODE_TARGET_WGS;
+constexpr long long kSplitTarget = MGQA_SPLIT_TARGET_WGS;
+constexpr int kMaxCounters = kSplitTarget > 256 ? (int)kSplitTarget : 256;  // leading counter block
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -50,6 +44,19 @@ int validate(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int win
 
 }  // namespace
 
+// Key band [lo, hi] of the query positions [q0, q0 + m_eff) (bottom-right aligned).
+static void block_band(int q0, int m_eff, int Lq, int Lkv, int causal, int window, int* lo, int* hi) {
+  const int off = Lkv - Lq;
+  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
+  *lo = 0;
+  *hi = Lkv - 1;
+  if (causal && pos_max < *hi) *hi = pos_max;
+  if (window > 0) {
+    if (pos_min - window + 1 > 0) *lo = pos_min - window + 1;
+    if (!causal && pos_max + window - 1 < *hi) *hi = pos_max + window - 1;
+  }
+}
+
 int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
               float softcap, int dtype, Plan* plan) {
   const int err = validate(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype);
@@ -59,57 +66,88 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   p.dqk = (d + 31) / 32;
   p.dv = (d <= 80 && d > 64) ? 5 : 2 * p.dqk;  // 72 and 80 use a 80-wide P.V
   const long long units = (long long)B * Hkv;
+  const long long rows_all = (long long)G * Lq;
+  const int max_nqb = p.dv <= kSplitWideMaxDv ? kSplitMaxNqb : kSplitMaxNqbWide;
 
-  if (G * Lq <= kMaxRowsDecode) {
-    p.path = kPathDecode;
-    p.keys_per_tile = kDecodeKeys;
-    p.rows_per_wg = kMaxRowsDecode;
-    p.nqb = 1;
-    const int off = Lkv - Lq;
-    const int key_lo = window > 0 ? (off - window + 1 > 0 ? off - window + 1 : 0) : 0;
-    const int t_begin = key_lo / kDecodeKeys;
-    const int t_end = (Lkv - 1) / kDecodeKeys + 1;
-    const int tiles = t_end - t_begin;
-    long long ns = (kTargetWGs + units - 1) / units;
-    if (ns > tiles) ns = tiles;
-    if (ns < 1) ns = 1;
-    const int tps = (int)((tiles + ns - 1) / ns);
-    ns = (tiles + tps - 1) / tps;
-    p.nsplit = (int)ns;
-    p.tiles_per_split = tps;
-    p.workgroups = units * ns;
-    if (ns > 1) {
-      const size_t nrows = (size_t)G * Lq;
-      const size_t o_bytes = (size_t)units * ns * nrows * (p.dv * 16) * sizeof(float);
-      const size_t ml_bytes = (size_t)units * ns * nrows * 2 * sizeof(float);
-      const size_t cnt_bytes = (size_t)units * sizeof(unsigned);
-      p.ws_cnt_off = 0;
-      p.ws_ml_off = align_up(cnt_bytes, 256);
-      p.ws_o_off = align_up(p.ws_ml_off + ml_bytes, 256);
-      p.ws_bytes = align_up(p.ws_o_off + o_bytes, 256);
-    }
-  } else {
+  // Prefill kernel: its 256-row block, when that still gives a workgroup per CU.
+  const int m_big = 16 * kPrefillWaves * kPrefillNqb / G;
+  const long long wgs_big = units * ((Lq + m_big - 1) / m_big);
+  if (rows_all > 16LL * max_nqb && wgs_big >= kCUs) {
     p.path = kPathPrefill;
     p.keys_per_tile = kPrefillKeys;
     p.nsplit = 1;
-    // The large block (MGQA_PREFILL_WAVES waves x MGQA_PREFILL_NQB 16-row
-    // blocks) when it still gives at least two workgroups per CU, else
-    // 4 waves x 16 rows.
-    const int big_rows = 16 * MGQA_PREFILL_WAVES * MGQA_PREFILL_NQB;
-    const int m_big = big_rows / G;
-    const long long wgs_big = units * ((Lq + m_big - 1) / m_big);
-    if (wgs_big >= 2 * kCUs) {
-      p.nqb = MGQA_PREFILL_NQB;
-      p.nwaves = MGQA_PREFILL_WAVES;
-    } else {
-      p.nqb = 1;
-      p.nwaves = 4;
-    }
+    p.nqb = kPrefillNqb;
+    p.nwaves = kPrefillWaves;
     p.rows_per_wg = 16 * p.nwaves * p.nqb;
-    const int m = p.rows_per_wg / G;
-    p.workgroups = units * ((Lq + m - 1) / m);
+    p.m = m_big;
+    p.n_pos_blk = (Lq + m_big - 1) / m_big;
+    p.workgroups = wgs_big;
+    *plan = p;
+    return MGQA_OK;
+  }
+
+  // Split-KV kernel.  Every row in one workgroup when they fit (decode and
+  // multi-token decode: K/V are read once per unit); otherwise the largest
+  // row block that still gives a workgroup per CU.  Then the key band is split
+  // across workgroups until about one workgroup per CU runs.
+  p.path = kPathSplit;
+  p.keys_per_tile = kSplitKeys;
+  p.nwaves = kSplitWaves;
+  if (rows_all <= 16LL * max_nqb) {
+    p.nqb = (int)((rows_all + 15) / 16);
+    p.m = Lq;
+  } else {
+    p.nqb = 1;
+    for (int nqb = max_nqb; nqb >= 1; --nqb) {
+      const int m = 16 * nqb / G;
+      if (m >= 1 && units * ((Lq + m - 1) / m) >= kSplitTarget) {
+        p.nqb = nqb;
+        break;
+      }
+    }
+    p.m = 16 * p.nqb / G;
+  }
+  p.rows_per_wg = 16 * p.nqb;
+  p.n_pos_blk = (Lq + p.m - 1) / p.m;
+  const long long groups = units * p.n_pos_blk;
+  long long ns = 1;
+  int tps = 1 << 30;  // one split: the whole band
+  if (groups < kSplitTarget) {
+    // Largest band (in tiles) of any position block (fewer than kSplitTarget blocks here).
+    int max_tiles = 1;
+    for (int pb = 0; pb < p.n_pos_blk; ++pb) {
+      const int q0 = pb * p.m;
+      const int m_eff = Lq - q0 < p.m ? Lq - q0 : p.m;
+      int lo, hi;
+      block_band(q0, m_eff, Lq, Lkv, causal, window, &lo, &hi);
+      const int tiles = hi / kSplitKeys - lo / kSplitKeys + 1;
+      if (tiles > max_tiles) max_tiles = tiles;
+    }
+    ns = (kSplitTarget + groups - 1) / groups;
+    if (ns > max_tiles) ns = max_tiles;
+    tps = (int)((max_tiles + ns - 1) / ns);
+    ns = (max_tiles + tps - 1) / tps;
+  }
+  p.nsplit = (int)ns;
+  p.tiles_per_split = tps;
+  p.workgroups = groups * ns;
+  if (ns > 1) {
+    const size_t nrows = (size_t)p.m * G;
+    const size_t o_bytes = (size_t)groups * ns * nrows * (p.dv * 16) * sizeof(float);
+    const size_t ml_bytes = (size_t)groups * ns * nrows * 2 * sizeof(float);
+    // Key splits happen only with fewer than kSplitTarget groups, so the
+    // counters of every plan fit the same leading kMaxCounters words: no plan
+    // writes partials there, and the counters a call leaves at zero stay zero
+    // for the next call on the same workspace, whatever its shape.
+    p.ws_cnt_off = 0;
+    p.ws_ml_off = align_up((size_t)kMaxCounters * sizeof(unsigned), 256);
+    p.ws_o_off = align_up(p.ws_ml_off + ml_bytes, 256);
+    p.ws_bytes = align_up(p.ws_o_off + o_bytes, 256);
   }
   if (p.workgroups >= (1LL << 31)) return MGQA_ERR_RANGE;
+  if (ns > 1 && groups > kMaxCounters) return MGQA_ERR_RANGE;  // cannot happen: see the counter layout
+  // 32-bit byte offsets of the partials inside the kernel.
+  if (p.ws_bytes >= (1ULL << 31)) return MGQA_ERR_RANGE;
   *plan = p;
   return MGQA_OK;
 }
@@ -140,24 +178,16 @@ static KernelArgs make_args(const Plan& p, const void* q, const void* k, const v
     a.c2 = (float)((double)softcap * log2e);
     a.beta = (float)(1.0 / ((double)softcap * sqrt((double)d)));
   }
-  if (p.path == kPathPrefill) {
-    a.m = p.rows_per_wg / a.G;
-    a.n_pos_blk = (Lq + a.m - 1) / a.m;
-    a.nsplit = 1;
-  } else {
-    const int off = Lkv - Lq;
-    const int key_lo = window > 0 ? (off - window + 1 > 0 ? off - window + 1 : 0) : 0;
-    a.t_begin = key_lo / kDecodeKeys;
-    a.t_end = (Lkv - 1) / kDecodeKeys + 1;
-    a.nsplit = p.nsplit;
-    a.tiles_per_split = p.tiles_per_split;
-    a.nrows = a.G * Lq;
-    if (ws) {
-      char* base = static_cast<char*>(ws);
-      a.ws_cnt = reinterpret_cast<unsigned*>(base + p.ws_cnt_off);
-      a.ws_ml = reinterpret_cast<float*>(base + p.ws_ml_off);
-      a.ws_o = reinterpret_cast<float*>(base + p.ws_o_off);
-    }
+  a.m = p.m;
+  a.n_pos_blk = p.n_pos_blk;
+  a.nsplit = p.nsplit;
+  a.tiles_per_split = p.tiles_per_split;
+  a.nrows = p.m * a.G;
+  if (ws) {
+    char* base = static_cast<char*>(ws);
+    a.ws_cnt = reinterpret_cast<unsigned*>(base + p.ws_cnt_off);
+    a.ws_ml = reinterpret_cast<float*>(base + p.ws_ml_off);
+    a.ws_o = reinterpret_cast<float*>(base + p.ws_o_off);
   }
   return a;
 }
@@ -243,7 +273,8 @@ int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void
   Plan p;
   const int err = make_plan(B, Hq, Hkv, Lq, length, d, causal, window, softcap, dtype, &p);
   if (err) return err;
-  if (ring_start >= 0 && p.path != kPathDecode) return MGQA_ERR_UNSUPPORTED;
+  if (ring_start >= 0 && (p.path != kPathSplit || p.n_pos_blk != 1 || p.nqb != 1))
+    return MGQA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return MGQA_ERR_ALIGN;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return MGQA_ERR_WORKSPACE;

@@ -7,17 +7,25 @@
 
 namespace mgqa {
 
-// Keys per staged tile.
-constexpr int kPrefillKeys = 64;   // prefill/encoder: every wave sweeps the whole tile
-#ifndef MGQA_DECODE_WAVES
-#define MGQA_DECODE_WAVES 8
+// Prefill kernels: 8 waves x 2 blocks of 16 rows, every wave sweeps whole
+// 64-key tiles.
+constexpr int kPrefillKeys = 64;
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillNqb = 2;
+// Split-KV kernel: waves per workgroup; each wave takes 32 keys of a tile.
+#ifndef MGQA_SPLIT_WAVES
+#define MGQA_SPLIT_WAVES 4
 #endif
-constexpr int kDecodeWaves = MGQA_DECODE_WAVES;  // split decode: waves per workgroup
-constexpr int kDecodeKeys = 32 * kDecodeWaves;    // each wave takes 32 keys of a tile
-constexpr int kThreads = 256;      // 4 wave64 per workgroup
-constexpr int kMaxRowsDecode = 16; // one 16-column MFMA block of (head, position) rows
+constexpr int kSplitWaves = MGQA_SPLIT_WAVES;
+constexpr int kSplitKeys = 32 * kSplitWaves;
+#ifndef MGQA_SPLIT_MAX_NQB
+#define MGQA_SPLIT_MAX_NQB 4
+#endif
+constexpr int kSplitMaxNqb = MGQA_SPLIT_MAX_NQB;  // 16-row blocks per workgroup, head size <= 96
+constexpr int kSplitMaxNqbWide = 2; // head size > 96 (register budget)
+constexpr int kSplitWideMaxDv = 6;  // P.V 16-column blocks up to which 3 and 4 row blocks exist
 
-enum Path { kPathPrefill = 0, kPathDecode = 1 };
+enum Path { kPathPrefill = 0, kPathSplit = 1 };
 
 // Everything a kernel needs, passed by value.
 struct KernelArgs {
@@ -25,9 +33,9 @@ struct KernelArgs {
   const void* k;
   const void* v;
   void* out;
-  float* ws_o;        // decode partial outputs [unit][split][nrows][dv_pad]
-  float* ws_ml;       // decode partial (max, sum) [unit][split][nrows][2]
-  unsigned* ws_cnt;   // decode arrival counters [unit]
+  float* ws_o;        // split partial outputs [group][split][nrows][dv_pad]
+  float* ws_ml;       // split partial (max, sum) [group][split][nrows][2]
+  unsigned* ws_cnt;   // split arrival counters [group]; group = unit * n_pos_blk + position block
   int Hq, Hkv, G, Lq, Lkv, d;
   long long kv_stride;  // elements between consecutive (batch, kv head) units of K and V
   int ring_start;       // -1: linear keys; else key j lives in slot (ring_start + j) % ring_slots
@@ -37,25 +45,24 @@ struct KernelArgs {
   float gamma;        // 2*log2(e)/(c*sqrt(d)): softcap exp argument
   float c2;           // c*log2(e): softcapped score bound in exponent units
   float beta;         // 1/(c*sqrt(d))
-  // prefill
   int m;              // query positions per workgroup
   int n_pos_blk;      // position blocks per (batch, kv head)
-  // decode
-  int nsplit;         // splits per unit
+  // split path
+  int nsplit;         // key splits per position block
   int tiles_per_split;
-  int t_begin;        // first key tile of the band (same for every unit)
-  int t_end;          // one past the last key tile
-  int nrows;          // G*Lq rows per unit
+  int nrows;          // m*G rows of a full position block
 };
 
 struct Plan {
   int path;
   int dqk;            // 32-wide head-size steps for Q.K^T
   int dv;             // 16-wide head-size blocks for P.V
-  int nqb;            // prefill: 16-row query blocks per wave
-  int nwaves;         // prefill: waves per workgroup
+  int nqb;            // 16-row query blocks per wave
+  int nwaves;         // waves per workgroup
   int rows_per_wg;
   int keys_per_tile;
+  int m;              // query positions per workgroup
+  int n_pos_blk;      // position blocks per (batch, kv head)
   int nsplit;
   int tiles_per_split;
   long long workgroups;

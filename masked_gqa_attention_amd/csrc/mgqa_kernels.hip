@@ -130,6 +130,55 @@ __device__ __forceinline__ void wait_vmem_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Butterfly steps across the four 16-lane groups of a wave (the lanes that
+// hold one MFMA column).  v_permlane16_swap / v_permlane32_swap applied to a
+// value and a copy of it leave, in each lane, the value and that of lane ^ 16
+// (lane ^ 32) in the two registers; the max or sum of the pair is the
+// butterfly step, with no LDS round trip.  The sum is the same in both lanes of
+// a pair.  (The two results are copied out as integers before the bit cast:
+// a bit cast applied directly to an element of the returned vector reads the
+// first element for both.)
+template <bool X32>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  unsigned r0, r1;
+  if constexpr (X32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+// (A compare and select: no NaN quieting of the bit-cast values needed.)
+__device__ __forceinline__ float xor16_max(float x) {
+  float a, b;
+  lane_pair<false>(x, a, b);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  float a, b;
+  lane_pair<true>(x, a, b);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  float a, b;
+  lane_pair<false>(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float a, b;
+  lane_pair<true>(x, a, b);
+  return a + b;
+}
+// Max / sum over the four lanes l % 16 == c of a column.
+__device__ __forceinline__ float col_max(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float col_sum(float x) { return xor32_sum(xor16_sum(x)); }
+
 // Visibility of global key `j` to a row at absolute key position `pos`.
 __device__ __forceinline__ bool key_visible(int j, int pos, int Lkv, int causal, int window) {
   bool ok = j < Lkv;
@@ -392,8 +441,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][hh][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = col_max(mx);
     float mxe;
     if (SOFTCAP) {
       // Same formula as the per-score path below, so the row maximum maps to
@@ -605,9 +653,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    float l = l_p[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = col_sum(l_p[qb]);
     if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, d, g4);
   }
 }
@@ -743,31 +789,32 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
 
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    float l = l_p[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = col_sum(l_p[qb]);
     if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, D, g4);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV decode kernel: one workgroup of NW waves per (unit = batch*Hkv +
-// kv head, split).  The 16 rows are (head of the group, position) pairs, head
-// fastest, nrows = G*Lq <= 16 of them real.  Each 32*NW-key tile is staged
-// once (K and V row-major, V read transposed); wave w takes keys
-// [32w, 32w+32) of it.  The wave states are merged in LDS, then the split's
-// partial is written, and the last split to arrive for the unit merges all
-// partials in split order and writes the output.
+// Split-KV kernel (decode, multi-token decode, short and mid-length
+// sequences): one workgroup of NW waves per (unit = batch*Hkv + kv head, block
+// of m query positions, key split).  Its rows are (position, head of the group)
+// pairs, head fastest: NQB blocks of 16, m*G <= 16*NQB of them real.  Each
+// 32*NW-key tile is staged once (K and V row-major, V read transposed); wave w
+// takes keys [32w, 32w+32) of it for all rows, so the key axis is split across
+// the waves.  The wave states are merged in LDS in wave order, one 16-row block
+// at a time.  With one split the merged rows are the output; otherwise the
+// split's partial is written and the last split to arrive for the block merges
+// all partials in split order.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NW, bool SOFTCAP, bool RING>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
+template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING>
+__global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KEYS = 32 * NW;
   constexpr int KP = DQK * 32 + 8;
   constexpr int VP = DV * 16 + 16;
   constexpr int DVP = DV * 16;
   constexpr int OP = DVP + 4;  // LDS pitch of the merged wave outputs (floats)
-  // K and V tiles; after the key loop the same bytes hold the wave outputs.
+  // K and V tiles; after the key loop the same bytes hold one row block's wave outputs.
   constexpr int TILE_BYTES = KEYS * (KP + VP) * 2;
   constexpr int MERGE_BYTES = NW * 16 * OP * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
@@ -780,59 +827,88 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x % a.nsplit;
-  const int unit = blockIdx.x / a.nsplit;
+  const int grp = blockIdx.x / a.nsplit;  // unit * n_pos_blk + position block
+  const int pblk = grp % a.n_pos_blk;
+  const int unit = grp / a.n_pos_blk;
   const int kvh = unit % a.Hkv, b = unit / a.Hkv;
   const int G = a.G, d = a.d;
   const int off = a.Lkv - a.Lq;
+  const int q0 = pblk * a.m;
+  const int m_eff = min(a.m, a.Lq - q0);
+  const int nrows = m_eff * G;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
-  const int pos_min = off, pos_max = off + a.Lq - 1;
-  const int t0 = a.t_begin + split * a.tiles_per_split;
-  const int t1 = min(a.t_end, t0 + a.tiles_per_split);
+  // Key band of this block of positions, in tiles, and this split's share.
+  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
+  int key_lo = 0, key_hi = a.Lkv - 1;
+  if (a.causal) key_hi = min(key_hi, pos_max);
+  if (a.window > 0) {
+    key_lo = max(0, pos_min - a.window + 1);
+    if (!a.causal) key_hi = min(key_hi, pos_max + a.window - 1);
+  }
+  const int t0 = key_lo / KEYS + split * a.tiles_per_split;
+  const int t1 = min(key_hi / KEYS + 1, t0 + a.tiles_per_split);
   RowTile<KEYS, DQK * 4, KP, NT> kt;
   RowTile<KEYS, DV * 2, VP, NT> vt;
   kt.init(d, tid);
   vt.init(d, tid);
-  auto fetch = [&](int k0) {
-    if (RING) {
-      kt.load_ring(kg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
-      vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
-    } else {
-      kt.load(kg, k0, a.Lkv, d);
-      vt.load(vg, k0, a.Lkv, d);
-    }
+  auto fetch_k = [&](int k0) {
+    if (RING) kt.load_ring(kg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
+    else kt.load(kg, k0, a.Lkv, d);
   };
-  if (t0 < t1) fetch(t0 * KEYS);
+  auto fetch_v = [&](int k0) {
+    if (RING) vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
+    else vt.load(vg, k0, a.Lkv, d);
+  };
+  if (t0 < t1) {
+    fetch_k(t0 * KEYS);
+    fetch_v(t0 * KEYS);
+  }
 
-  // This lane's row (column c16 of the single query block).
-  const int r = c16;
-  const bool rok = r < a.nrows;
-  const int pl = r / G, hr = r % G;
-  const int head = kvh * G + hr;
-  const size_t roff = (((size_t)b * a.Hq + head) * a.Lq + (rok ? pl : 0)) * d;
-  u32x4 qf[1][DQK];
-  int qpos[1] = {pl + off};
-  load_q<DQK>(qf[0], qg + roff, rok, d, g4);
-
-  float m_e[1] = {kNegInf}, l_p[1] = {0.f};
-  f32x4 o[1][DV];
+  // This lane's rows: column c16 of each 16-row block.
+  u32x4 qf[NQB][DQK];
+  int qpos[NQB];
 #pragma unroll
-  for (int db = 0; db < DV; ++db) o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int r = 16 * qb + c16;
+    const bool rok = r < nrows;
+    const int pl = r / G, hr = r % G;
+    const size_t roff = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (rok ? q0 + pl : 0)) * d;
+    qpos[qb] = q0 + pl + off;
+    load_q<DQK>(qf[qb], qg + roff, rok, d, g4);
+  }
+
+  float m_e[NQB], l_p[NQB];
+  f32x4 o[NQB][DV];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_e[qb] = kNegInf;
+    l_p[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   u32x4 kf_unused[2][DQK];
   for (int t = t0; t < t1; ++t) {
     const int k0 = t * KEYS;
     __syncthreads();  // every wave is done with the previous tile
+    // Each half of the staging registers is refilled with the next tile as
+    // soon as it is in LDS, so loads stay in flight while the other half is
+    // written, and the next tile flies during this one.
+    const bool more = t + 1 < t1;
     kt.store(Ks, tid);
+    if (more) fetch_k(k0 + KEYS);
     vt.store(Vs, tid);
-    if (t + 1 < t1) fetch(k0 + KEYS);  // registers are free again: next tile flies during this one
+    if (more) fetch_v(k0 + KEYS);
     __syncthreads();
-    // Full-tile test on this wave's 32 keys.
+    // This wave's 32 keys: skipped when wholly outside the band, unmasked
+    // when wholly inside it.
     const int w0 = k0 + 32 * wave;
+    if (w0 > key_hi || w0 + 31 < key_lo) continue;
     bool full = w0 + 32 <= a.Lkv;
     if (a.causal) full = full && (w0 + 31 <= pos_min);
     if (a.window > 0) {
@@ -840,90 +916,79 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
       if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
     }
     if (full)
-      tile_step<T, DQK, DV, 1, KP, VP, false, SOFTCAP, false, false, false>(
+      tile_step<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, false, false, false>(
           Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
     else
-      tile_step<T, DQK, DV, 1, KP, VP, false, SOFTCAP, true, false, false>(
+      tile_step<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, true, false, false>(
           Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
   }
 
-  // ---- merge the wave states (fixed order) ------------------------------------
-  __syncthreads();  // every wave is done reading the tiles that wo overwrites
-  float l = l_p[0];
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (g4 == 0) {
-    wm[wave][c16] = m_e[0];
-    wl[wave][c16] = l;
-  }
-#pragma unroll
-  for (int db = 0; db < DV; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wo[wave][c16 * OP + 16 * db + 4 * g4 + i] = o[0][db][i];
-  __syncthreads();
-
-  // Thread -> float4 chunks q = tid + NT*j of the [nrows][DVP] output block:
-  // row q / CPR, columns 4*(q % CPR) .. +3, so a wave touches contiguous memory.
+  // ---- merge the wave states (fixed order), one 16-row block at a time --------
+  // Thread -> float4 chunks q = tid + NT*j of a [16][DVP] block: row q / CPR,
+  // columns 4*(q % CPR) .. +3, so a wave touches contiguous memory.
   constexpr int CPR = DVP / 4;
   constexpr int JN = (16 * CPR + NT - 1) / NT;
-  const int nch = a.nrows * CPR;
-  float M[JN], L[JN];
-  f32x4 acc[JN];
+  const int rstride = a.nrows;  // rows of a full block: partial layout stride
+  const int pidx = (grp * a.nsplit + split) * rstride;
+  const uint32_t o_bytes = (uint32_t)gridDim.x * rstride * DVP * 4;
+  const uint32_t ml_bytes = (uint32_t)gridDim.x * rstride * 8;
+  const auto rs_o = make_rsrc(a.ws_o, o_bytes);
+  const auto rs_ml = make_rsrc(a.ws_ml, ml_bytes);
 #pragma unroll
-  for (int j = 0; j < JN; ++j) {
-    const int q = tid + j * NT;
-    const int row = min(q / CPR, 15), c4 = q % CPR;
-    M[j] = kNegInf;
-    L[j] = 0.f;
-    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M[j] = fmaxf(M[j], wm[w][row]);
-    if (M[j] != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = fast_exp2(wm[w][row] - M[j]);
-        L[j] += f * wl[w][row];
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&wo[w][row * OP + 4 * c4]);
-        acc[j] += f * x;
-      }
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (16 * qb >= nrows) break;
+    __syncthreads();  // tiles (or the previous block's outputs) are no longer read
+    const float l = col_sum(l_p[qb]);
+    if (g4 == 0) {
+      wm[wave][c16] = m_e[qb];
+      wl[wave][c16] = l;
     }
-  }
+#pragma unroll
+    for (int db = 0; db < DV; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[wave][c16 * OP + 16 * db + 4 * g4 + i] = o[qb][db][i];
+    __syncthreads();
 
-  if (a.nsplit == 1) {
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
       const int q = tid + j * NT;
-      const int row = q / CPR, c4 = q % CPR;
-      if (q < nch && 4 * c4 < d) {
-        const float inv = 1.0f / L[j];
-        const size_t oo = (((size_t)b * a.Hq + kvh * G + row % G) * a.Lq + row / G) * d + 4 * c4;
-        *reinterpret_cast<u32x2*>(og + oo) =
-            u32x2{Elem<T>::pack2(acc[j][0] * inv, acc[j][1] * inv), Elem<T>::pack2(acc[j][2] * inv, acc[j][3] * inv)};
+      const int row = min(q / CPR, 15), c4 = q % CPR;
+      const int r = 16 * qb + row;
+      if (q >= 16 * CPR || r >= nrows) continue;
+      float M = kNegInf, L = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][row]);
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = fast_exp2(wm[w][row] - M);
+          L += f * wl[w][row];
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&wo[w][row * OP + 4 * c4]);
+          acc += f * x;
+        }
+      }
+      if (a.nsplit == 1) {
+        if (4 * c4 < d) {
+          const float inv = 1.0f / L;
+          const size_t oo = (((size_t)b * a.Hq + kvh * G + r % G) * a.Lq + q0 + r / G) * d + 4 * c4;
+          *reinterpret_cast<u32x2*>(og + oo) =
+              u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
+        }
+      } else {
+        // This split's partial, with device-coherent stores.
+        st_dev16(rs_o, ((pidx + r) * DVP + 4 * c4) * 4, acc);
+        if (c4 == 0) st_dev8(rs_ml, (pidx + r) * 8, f32x2{M, L});
       }
     }
-    return;
   }
+  if (a.nsplit == 1) return;
 
-  // ---- write this split's partial (device-coherent stores) -----------------------
-  const uint32_t o_bytes = (uint32_t)gridDim.x * a.nrows * DVP * 4;
-  const uint32_t ml_bytes = (uint32_t)gridDim.x * a.nrows * 8;
-  const auto rs_o = make_rsrc(a.ws_o, o_bytes);
-  const auto rs_ml = make_rsrc(a.ws_ml, ml_bytes);
-  const int pidx = (unit * a.nsplit + split) * a.nrows;
-#pragma unroll
-  for (int j = 0; j < JN; ++j) {
-    const int q = tid + j * NT;
-    const int row = q / CPR, c4 = q % CPR;
-    if (q < nch) {
-      st_dev16(rs_o, ((pidx + row) * DVP + 4 * c4) * 4, acc[j]);
-      if (c4 == 0) st_dev8(rs_ml, (pidx + row) * 8, f32x2{M[j], L[j]});
-    }
-  }
   wait_vmem_done();
   __syncthreads();
   if (tid == 0) {
     const unsigned prev =
-        __hip_atomic_fetch_add(a.ws_cnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.ws_cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == (unsigned)(a.nsplit - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -933,9 +998,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
   // Online merge over groups of 16 splits; every load of a group is issued
   // before any of them is used.
   constexpr int CHUNK = 16;
-  const int base = unit * a.nsplit * a.nrows;
+  constexpr int JM = (16 * NQB * CPR + NT - 1) / NT;
+  const int nch = nrows * CPR;
+  const int base = grp * a.nsplit * rstride;
 #pragma unroll
-  for (int j = 0; j < JN; ++j) {
+  for (int j = 0; j < JM; ++j) {
     const int q = tid + j * NT;
     if (q >= nch) continue;
     const int row = q / CPR, c4 = q % CPR;
@@ -947,7 +1014,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
 #pragma unroll
       for (int jj = 0; jj < CHUNK; ++jj) {
         const int sp = min(s0 + jj, a.nsplit - 1);
-        const int pr = base + sp * a.nrows + row;
+        const int pr = base + sp * rstride + row;
         ml[jj] = ld_dev8(rs_ml, pr * 8);
         x[jj] = ld_dev16(rs_o, (pr * DVP + 4 * c4) * 4);
       }
@@ -971,12 +1038,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(KernelArgs a) {
     }
     if (4 * c4 < d) {
       const float inv = 1.0f / Lg;
-      const size_t oo = (((size_t)b * a.Hq + kvh * G + row % G) * a.Lq + row / G) * d + 4 * c4;
+      const size_t oo = (((size_t)b * a.Hq + kvh * G + row % G) * a.Lq + q0 + row / G) * d + 4 * c4;
       *reinterpret_cast<u32x2*>(og + oo) =
           u32x2{Elem<T>::pack2(og4[0] * inv, og4[1] * inv), Elem<T>::pack2(og4[2] * inv, og4[3] * inv)};
     }
   }
-  if (tid == 0) __hip_atomic_store(a.ws_cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(a.ws_cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_kernel(uint32_t* p, size_t n) {
@@ -987,24 +1054,37 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the instantiated shapes.
 // ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, int NQB, bool SOFTCAP>
+static void launch_split(const dim3& grid, const KernelArgs& args, hipStream_t st) {
+  const dim3 block(64 * kSplitWaves);
+  if (NQB == 1 && args.ring_start >= 0)
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, kSplitWaves, SOFTCAP, true>), grid, block, 0, st, args);
+  else
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, kSplitWaves, SOFTCAP, false>), grid, block, 0, st,
+                       args);
+}
+
 template <typename T, int DQK, int DV, bool SOFTCAP>
 static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStream_t st) {
-  const dim3 block(kThreads);
   const dim3 grid((unsigned)plan.workgroups);
-  if (plan.path == kPathDecode) {
-    if (args.ring_start >= 0)
-      hipLaunchKernelGGL((decode_kernel<T, DQK, DV, kDecodeWaves, SOFTCAP, true>), grid,
-                         dim3(64 * kDecodeWaves), 0, st, args);
-    else
-      hipLaunchKernelGGL((decode_kernel<T, DQK, DV, kDecodeWaves, SOFTCAP, false>), grid,
-                         dim3(64 * kDecodeWaves), 0, st, args);
-  } else if (plan.nwaves == 8 && plan.nqb == 2) {
-    if (args.d == 128)
-      hipLaunchKernelGGL((prefill128_kernel<T, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
-    else
-      hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
+  if (plan.path == kPathSplit) {
+    switch (plan.nqb) {
+      case 1: launch_split<T, DQK, DV, 1, SOFTCAP>(grid, args, st); break;
+      case 2: launch_split<T, DQK, DV, 2, SOFTCAP>(grid, args, st); break;
+      case 3:
+        if constexpr (DV <= kSplitWideMaxDv) launch_split<T, DQK, DV, 3, SOFTCAP>(grid, args, st);
+        else return hipErrorInvalidValue;
+        break;
+      case 4:
+        if constexpr (DV <= kSplitWideMaxDv) launch_split<T, DQK, DV, 4, SOFTCAP>(grid, args, st);
+        else return hipErrorInvalidValue;
+        break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (args.d == 128) {
+    hipLaunchKernelGGL((prefill128_kernel<T, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 1, 4, SOFTCAP>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   }
   return hipGetLastError();
 }

@@ -109,6 +109,19 @@ CASES = [
     Case("onehot_decode_window", 1, 8, 1, 1, 128, 128, causal=True, window=50, kind="onehot", seed=45),
     Case("const_v_prefill", 1, 8, 2, 90, 90, 72, causal=True, window=20, softcap=5.0, kind="const", seed=46),
     Case("const_v_decode", 1, 4, 1, 2, 700, 128, causal=True, kind="const", seed=47),
+    # split-KV kernel with several 16-row blocks per workgroup (position blocks
+    # of 16*nqb/G positions), with and without key splits across workgroups
+    Case("split_nqb4_d64_g2", 2, 16, 8, 512, 600, 64, causal=True, seed=50),
+    Case("split_nqb3_d72_fp16", 1, 18, 18, 700, 700, 72, dtype="fp16", seed=51),
+    Case("split_nqb2_d128_window_cap", 1, 16, 16, 512, 512, 128, causal=True, window=100, softcap=30.0,
+         seed=52),
+    Case("split_nqb2_g8_d128", 1, 32, 4, 256, 300, 128, causal=True, seed=53),
+    Case("split_multitoken_g4_lq16_d64", 1, 8, 2, 16, 2000, 64, causal=True, seed=54),
+    Case("split_multitoken_g8_lq4_cap", 2, 16, 2, 4, 3000, 128, causal=True, softcap=20.0, seed=55),
+    Case("split_multitoken_g2_lq24_d96", 1, 4, 2, 24, 1100, 96, causal=True, window=400, seed=56),
+    # prefill kernel (256-row workgroups), full parity
+    Case("prefill_big_g16_d128", 1, 256, 16, 256, 256, 128, causal=True, window=90, seed=57),
+    Case("prefill_big_g16_d96_noncausal", 1, 256, 16, 256, 200, 96, seed=58),
 ]
 
 CASES_BY_NAME = {c.name: c for c in CASES}

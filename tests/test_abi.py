@@ -129,7 +129,7 @@ def test_attn_fwd_validation_codes():
 def test_non_causal_longer_query_is_allowed_in_plan():
     # No mask and no window: every key is visible to every row, Lq > Lkv is fine.
     rc, info = _lib.attn_plan(1, 2, 1, 100, 10, 64, 0, 0, 0.0)
-    assert rc == 0 and info["path"] == 0
+    assert rc == 0 and info["workgroups"] >= 1
 
 
 def test_plans_for_workloads():
@@ -157,14 +157,21 @@ def test_plans_for_workloads():
 
 
 def test_workspace_layout_fits():
-    # The workspace size covers partials for every split, row and padded column.
-    for (B, Hq, Hkv, Lq, Lkv, d) in [(8, 32, 8, 1, 8192, 128), (4, 64, 4, 1, 32768, 128),
-                                     (3, 12, 4, 4, 5000, 72), (1, 16, 1, 1, 129, 64)]:
-        rc, info = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, 1, 0, 0.0)
+    # The workspace covers the fixed 1 KiB counter block plus partials for
+    # every position block, split, row and padded column.
+    for (B, Hq, Hkv, Lq, Lkv, d, causal) in [(8, 32, 8, 1, 8192, 128, 1), (4, 64, 4, 1, 32768, 128, 1),
+                                             (3, 12, 4, 4, 5000, 72, 1), (1, 16, 1, 1, 129, 64, 1),
+                                             (2, 16, 2, 100, 333, 128, 1), (1, 8, 2, 16, 2000, 64, 1),
+                                             (1, 3, 3, 150, 150, 72, 0)]:
+        rc, info = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, causal, 0, 0.0)
         assert rc == 0
         if info["nsplit"] > 1:
             G = Hq // Hkv
-            need = B * Hkv * info["nsplit"] * G * Lq * (info["d_pv_pad"] + 2) * 4 + B * Hkv * 4
+            rows = info["rows_per_wg"]
+            groups = info["workgroups"] // info["nsplit"]
+            assert groups < 256  # the counters fit the fixed block
+            m = min(rows // G, Lq)
+            need = 1024 + groups * info["nsplit"] * m * G * (info["d_pv_pad"] + 2) * 4
             assert info["workspace_bytes"] >= need
         else:
             assert info["workspace_bytes"] == 0

@@ -94,6 +94,46 @@ def test_attn_fwd_self_allocating_matches_ex():
         assert T.equal(a.view(T.int16), b.view(T.int16))
 
 
+def test_workspace_reuse_across_shapes():
+    """One workspace serves calls of different shapes in turn without being
+    cleared: a split decode with a large partial region, then shapes with many
+    row blocks and key splits (more arrival counters), then the decode again.
+    Each result must equal, bit for bit, the same call on a fresh zero-filled
+    workspace."""
+    import torch as T
+    from masked_gqa_attention_amd import _lib
+    from .cases import CASES_BY_NAME
+    from .gpu_util import to_device
+    names = ["decode_g4_kv3000", "prefill_causal_g8_bottomright", "split_multitoken_g8_lq4_cap",
+             "decode_g4_kv3000", "prefill_causal_g8_bottomright"]
+    sizes = []
+    for name in set(names):
+        c = CASES_BY_NAME[name]
+        sizes.append(_lib.attn_workspace_bytes(c.B, c.Hq, c.Hkv, c.Lq, c.Lkv, c.d, c.causal, c.window))
+    shared = T.zeros(max(sizes), dtype=T.uint8, device="cuda")
+    stream = T.cuda.current_stream().cuda_stream
+
+    def call(c, tensors, ws):
+        q, k, v = tensors
+        out = T.empty_like(q)
+        nbytes = _lib.attn_workspace_bytes(c.B, c.Hq, c.Hkv, c.Lq, c.Lkv, c.d, c.causal, c.window)
+        assert nbytes > 0
+        rc = _lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), c.B, c.Hq,
+                              c.Hkv, c.Lq, c.Lkv, c.d, c.causal, c.window, c.softcap,
+                              _lib.MGQA_BF16, ws.data_ptr(), ws.numel(), stream)
+        assert rc == 0, _lib.error_string(rc)
+        return out
+
+    for name in names:
+        c = CASES_BY_NAME[name]
+        announce(f"workspace reuse {name}")
+        tensors = [to_device(a, c.dtype) for a in make_inputs(c)]
+        got = call(c, tensors, shared)
+        fresh = call(c, tensors, T.zeros(max(sizes), dtype=T.uint8, device="cuda"))
+        T.cuda.synchronize()
+        assert T.equal(got.view(T.int16), fresh.view(T.int16)), name
+
+
 def test_suffix_consistency_decode_vs_prefill():
     """Bottom-right alignment across the two kernels: decode of the last
     query row equals the last row of a full prefill, and a 4-row chunk equals
