@@ -36,7 +36,7 @@ MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 MFMA
 LLC_BYTES = 256 * 1024 * 1024    # MI355X last-level (Infinity) cache
 COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate byte counters
 KERNEL_SRC = os.path.join(ROOT, "masked_gqa_attention_amd", "csrc", "mgqa_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_decode_gqa4_kv8192.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_splitkv_kernel_decode_gqa4_kv8192.json")
 
 
 def log(msg):
