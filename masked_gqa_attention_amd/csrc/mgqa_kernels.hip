@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mgqa_internal.h"
 
 namespace mgqa {
@@ -52,9 +54,6 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
-#ifndef MGQA_EARLY_FRAG
-#define MGQA_EARLY_FRAG false
-#endif
 // Lazy rescale threshold in base-2 exponent units.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -295,14 +294,27 @@ struct RowTile {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16-byte buffer load per lane that writes LDS directly: lane l's bytes land
-// at lds + 16*l (the base must be the same for the whole wave).
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0,
-                                           0, 0);
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Raw buffer descriptor words (base, stride 0, num_records = bytes, the same
+// format word as make_rsrc) for the inline-assembly load below.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
 }
 
-__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// The same 16-byte direct-to-LDS buffer load, written as inline assembly so
+// that the compiler does not track it: the compiler treats a direct-to-LDS
+// load as a store to any LDS location and makes every later LDS read wait
+// for it.  Here the caller orders the loads and the reads itself, with an
+// explicit vmcnt wait and a workgroup barrier before the stage is read.  The
+// instruction has no register result; its operands are read at issue.
+__device__ __forceinline__ void lds_dma16_async(const u32x4& rs, uint16_t* lds, int voff) {
+  const uint32_t m0 = wave_uniform(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  // (s_nop: one wait state between the write of M0 and the load that reads it.)
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(m0) : "memory");
+}
+
 
 // Transposed 4-key x 1-column read (see above); returns the 4 keys of this
 // lane's column as two packed dwords.
@@ -641,7 +653,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
     }
     // Two 32-key steps per tile; K fragments of the second step are read
     // during the first step's products.
-    tile_pair<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, MGQA_EARLY_FRAG>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16,
+    tile_pair<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, false>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16,
                                                         g4);
     if (t + 1 < t_end) {
       uint16_t* nxt = smem + (cur ^ 1) * STAGE;
@@ -659,31 +671,223 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill / encoder kernel for head size 128: same work split as
-// prefill_kernel, but K and V tiles go straight from HBM to LDS with buffer
-// loads that write LDS (16 bytes per lane, a wave writes 1 KB = 4 dense rows),
-// through swizzled slots (see read_kfrag).  Keys past Lkv are outside the
-// descriptor's range and land as zeros.  Three LDS stages: tile t+2 is fetched
-// while tile t is in use; one barrier per tile.  No registers or vector ALU
-// work go into staging.
+// Software-pipelined prefill for head size 128.
+//
+// The key axis is walked in 32-key steps j.  Step j runs, in straight-line
+// code,
+//   * the fp32 softmax arithmetic of the scores S_j (vector ALU),
+//   * the MFMA products of the next step's scores S_{j+1} = K_{j+1} Q^T,
+//   * the MFMA products of the previous step's O^T += V_{j-1}^T P_{j-1}^T,
+// so the matrix cores work while the vector ALU computes probabilities.  The
+// row sum of P is taken on the matrix cores too (an all-ones A operand), from
+// the same 16-bit probabilities that enter P.V.
+//
+// Fixed reference (FIXREF): with a softcap c, every score lies in [-c, c], so
+// exp2 of a softcapped score (base-2 units) minus c*log2(e) - 40 lies in
+// [2^(40 - 2c log2 e), 2^40].  For c <= 57.5 that is inside the normal range
+// of fp32 and bf16: no running maximum and no rescale are needed.  Otherwise
+// the running maximum is kept with the lazy rescale.
+//
+// LDS: four stages of one 64-key tile, all K tiles first, then all V tiles,
+// filled by direct global-to-LDS loads.  Tile t+3 is requested once every
+// wave is past the first half of tile t, so each tile has two tiles of time
+// to land.  The tile loop is unrolled over the four stages, so every fragment
+// read is one of twelve per-lane base addresses plus a constant offset.
 // ---------------------------------------------------------------------------
-template <typename T, int NQB, int NWAVES, bool SOFTCAP>
-__global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
-  constexpr int DQK = 4, DV = 8, D = 128;
-  constexpr int KEYS = kPrefillKeys;
-  constexpr int TILE = KEYS * D;          // elements of one K (or V) tile
-  constexpr int STAGE = 2 * TILE;
-  constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row DMA instructions per wave per tensor
-  static_assert(IPW * NWAVES * 4 == KEYS, "tile rows must split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
+constexpr int kPipeStages = 4;
+constexpr int kPipeTile = 64 * 128;                    // elements of one K or V tile
+constexpr int kPipeVRegion = kPipeStages * kPipeTile;  // first V tile (elements)
+
+template <typename T>
+struct OnesOperand;
+template <>
+struct OnesOperand<__bf16> {
+  static constexpr uint32_t kPair = 0x3F803F80u;  // two bf16 1.0
+};
+template <>
+struct OnesOperand<_Float16> {
+  static constexpr uint32_t kPair = 0x3C003C00u;  // two fp16 1.0
+};
+
+// Per-lane fragment offsets (elements): ka[t] -> K row c16, chunk 4t+g4 of
+// tile row 0 (swizzled slot); va[db] -> the transposed V read of columns
+// 16*db.. of tile row 4*g4 + c16/4.
+struct PipeAddr {
+  int ka[4];
+  int va[8];
+};
+
+// Probabilities of 4 scores (one 16-key half of one 16-row block), fp32.
+template <bool SOFTCAP>
+__device__ __forceinline__ void pipe_probs(const f32x4& x, float mref, const KernelArgs& a, float (&p)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (SOFTCAP) {
+      const float r = fast_rcp(fast_exp2(x[i] * a.gamma) + 1.0f);
+      p[i] = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
+    } else {
+      p[i] = fast_exp2(__builtin_fmaf(x[i], a.alpha, -mref));
+    }
+  }
+}
+
+// Keeps the compiler from moving the computation of v across this point
+// (it sees v as read and rewritten here).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(f32x4& v) { asm volatile("" : "+v"(v)); }
+
+// One 32-key step.  Kst + KOFF: step j+1's K rows (stage array, tile row),
+// Vst + VOFF: step j-1's V rows.  sc: scores of step j (in), sn: of
+// step j+1 (out); pp: probabilities of step j-1 (in), pc: of step j (out).
+// Visibility of key kglob + 16*hh + 4*g4 + i to row block qb:
+// (unsigned)(ubase[qb] + 16*hh + i) <= span[qb]; MASK is false when every
+// key of the step is visible to every row of the workgroup.
+//
+// The products and the exponentials form one straight-line block of four
+// quarters, each with 8 MFMAs (two V and two K fragments) and the
+// probabilities of 4 scores, so that few fragments are live at a time.  The
+// mask (partial steps only) is applied after that block.  With a running
+// maximum, the new maximum is taken first (the exponentials use it at once)
+// and the accumulators are rescaled at the end, after the products of step
+// j-1 -- whose probabilities used the old maximum -- are in.
+template <typename T, bool SOFTCAP, bool FIXREF, int KOFF, int VOFF>
+__device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const uint16_t* Vst, const PipeAddr& ad,
+                                          f32x4 (&sc)[2][2], f32x4 (&sn)[2][2],
+                                          const u32x4 (&pp)[2], u32x4 (&pc)[2], const u32x4 (&qf)[2][4],
+                                          f32x4 (&o)[2][8], f32x4 (&ls)[2], float (&m_e)[2],
+                                          const int (&ubase)[2], const int (&span)[2], const KernelArgs& a) {
+  const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
+                      OnesOperand<T>::kPair};
+  float mref[2], resc[2] = {1.0f, 1.0f};
+  if constexpr (FIXREF) {
+    mref[0] = mref[1] = a.c2 - 40.0f;
+  } else {
+    if (mask) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((unsigned)(ubase[qb] + 16 * hh + i) > (unsigned)span[qb]) sc[qb][hh][i] = kNegInf;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = fmaxf(fmaxf(fmaxf(sc[qb][0][0], sc[qb][0][1]), fmaxf(sc[qb][0][2], sc[qb][0][3])),
+                       fmaxf(fmaxf(sc[qb][1][0], sc[qb][1][1]), fmaxf(sc[qb][1][2], sc[qb][1][3])));
+      mx = col_max(mx);
+      float mxe;
+      if (SOFTCAP)
+        mxe = (mx == kNegInf) ? kNegInf
+                              : __builtin_fmaf(fast_rcp(fast_exp2(mx * a.gamma) + 1.0f), -2.0f * a.c2, a.c2);
+      else
+        mxe = mx * a.alpha;
+      if (mxe > m_e[qb] + kRescaleSlack) {
+        resc[qb] = fast_exp2(m_e[qb] - mxe);  // 0 when m_e was -inf
+        m_e[qb] = mxe;
+      }
+      mref[qb] = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Fragments of quarter k: V columns 32k..32k+31 of step j-1 and K chunks
+  // 2(k%2), 2(k%2)+1 of key rows 16(k/2).. of step j+1.  Each quarter reads
+  // the next quarter's fragments before its own products.
+  auto frags = [&](int k, u32x4 (&vf)[2], u32x4 (&kf)[2]) {
+    const int hh = k >> 1, t0 = 2 * (k & 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint16_t* v0 = Vst + ad.va[2 * k + e] + VOFF;
+      const u32x2 lo = lds_read_tr4(v0);
+      const u32x2 hi = lds_read_tr4(v0 + 16 * 128);
+      vf[e] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      kf[e] = *reinterpret_cast<const u32x4*>(Kst + ad.ka[t0 + e] + KOFF + hh * 16 * 128);
+    }
+  };
+  float p[2][2][4];
+  u32x4 fr[2][2][2];  // [buffer][V, K][e]
+  frags(0, fr[0][0], fr[0][1]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int hh = k >> 1, t0 = 2 * (k & 1);
+    const int qs = k >> 1, hs = k & 1;  // scores whose probabilities this quarter computes
+    const int cur = k & 1;
+    pin(sc[qs][hs]);
+    if (k < 3) frags(k + 1, fr[cur ^ 1][0], fr[cur ^ 1][1]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[qb][2 * k + e] = Elem<T>::mfma(fr[cur][0][e], pp[qb], o[qb][2 * k + e]);
+    if (k == 3) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) ls[qb] = Elem<T>::mfma(ones, pp[qb], ls[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x4 acc = (k & 1) ? sn[qb][hh] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) acc = Elem<T>::mfma(fr[cur][1][e], qf[qb][t0 + e], acc);
+      sn[qb][hh] = acc;
+    }
+    pipe_probs<SOFTCAP>(sc[qs][hs], mref[qs], a, p[qs][hs]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pin(p[qs][hs][i]);
+    // Next quarter's fragment reads first, then one MFMA per three vector-ALU ops.
+    if (k < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int g = 0; g < 10; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (mask) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((unsigned)(ubase[qb] + 16 * hh + i) > (unsigned)span[qb]) p[qb][hh][i] = 0.f;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+    pc[qb] = u32x4{Elem<T>::pack2(p[qb][0][0], p[qb][0][1]), Elem<T>::pack2(p[qb][0][2], p[qb][0][3]),
+                   Elem<T>::pack2(p[qb][1][0], p[qb][1][1]), Elem<T>::pack2(p[qb][1][2], p[qb][1][3])};
+
+  if constexpr (!FIXREF) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      if (resc[qb] != 1.0f) {
+        ls[qb] *= resc[qb];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[qb][db] *= resc[qb];
+      }
+  }
+}
+
+template <typename T, bool SOFTCAP, bool FIXREF>
+__global__ __launch_bounds__(512) void prefill_pipe_kernel(KernelArgs a) {
+  constexpr int NWAVES = 8, D = 128, KEYS = 64, TILE = kPipeTile;
+  constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row direct-to-LDS loads per wave per tensor
+  static_assert(IPW == 2, "the wait counts below assume two loads per tensor per wave");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kPipeStages * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
 
   const int bid = blockIdx.x;
-  const int pblk = bid % a.n_pos_blk;
-  const int unit = bid / a.n_pos_blk;  // b * Hkv + kvh
+  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
+  // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
+  // range of (unit, position block) pairs: the blocks of one unit then share
+  // their K/V tiles in one L2.
+  int lin = bid;
+  if ((gridDim.x & 7) == 0) lin = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+  const int pblk = lin % a.n_pos_blk;
+  const int unit = lin / a.n_pos_blk;  // b * Hkv + kvh
   const int kvh = unit % a.Hkv, b = unit / a.Hkv;
   const int G = a.G;
   const int q0 = pblk * a.m;
@@ -695,7 +899,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
-  // Key band of this block of positions.
+  // Key band of this block of positions, in tiles.
   const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
   int key_lo = 0, key_hi = a.Lkv - 1;
   if (a.causal) key_hi = min(key_hi, pos_max);
@@ -705,9 +909,27 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
   }
   const int t_begin = key_lo / KEYS, t_end = key_hi / KEYS + 1;
 
-  // DMA lane offsets (bytes from the tile's first key), loop invariant: lane
-  // fills slot lane%16 of row 4*instr + lane/16 with the chunk the swizzle
-  // puts there.
+  // Q first: the direct-to-LDS loads are counted after it, so waiting for
+  // the first tile also waits for Q.
+  u32x4 qf[2][4];
+  int rconst[2], span[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = (wave * 2 + qb) * 16 + c16;
+    const int pl = r / G, hr = r % G;
+    const bool ok = pl < m_eff;
+    const int pos = q0 + pl + off;
+    const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (ok ? q0 + pl : 0)) * D;
+    load_q<4>(qf[qb], qg + ro, ok, D, g4);
+    // Visible keys of this row: [lo, hi].
+    const int lo = a.window > 0 ? pos - a.window + 1 : 0;
+    int hi = a.Lkv - 1;
+    if (a.causal) hi = min(hi, pos);
+    else if (a.window > 0) hi = min(hi, pos + a.window - 1);
+    rconst[qb] = 4 * g4 - lo;
+    span[qb] = hi - lo;
+  }
+
   int voffK[IPW], voffV[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
@@ -715,82 +937,158 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill128_kernel(KernelArgs a) {
     voffK[j] = (row * D + ((slot ^ (row & 15)) << 3)) * 2;
     voffV[j] = (row * D + ((slot ^ (2 * (row & 7))) << 3)) * 2;
   }
-  auto fetch = [&](int t, int st) {
-    const int k0 = t * KEYS;
-    const uint32_t bytes = (uint32_t)(a.Lkv - k0) * (uint32_t)(D * 2);
-    const auto rk = make_rsrc(kg + (size_t)k0 * D, bytes);
-    const auto rv = make_rsrc(vg + (size_t)k0 * D, bytes);
+  auto fetch = [&](int t, uint16_t* kst, uint16_t* vst) {
+    // (Forced into scalar registers: the descriptor must be uniform.)
+    const int k0 = wave_uniform(t * KEYS);
+    const uint32_t bytes = (uint32_t)wave_uniform((a.Lkv - k0) * (D * 2));
+    const u32x4 rk = raw_rsrc(kg + (size_t)k0 * D, bytes);
+    const u32x4 rv = raw_rsrc(vg + (size_t)k0 * D, bytes);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      uint16_t* dk = smem + st * STAGE + (wave * IPW + j) * 4 * D;
-      lds_dma16(rk, dk, voffK[j]);
-      lds_dma16(rv, dk + TILE, voffV[j]);
+      const int row0 = (wave * IPW + j) * 4 * D;
+      lds_dma16_async(rk, kst + row0, voffK[j]);
+      lds_dma16_async(rv, vst + row0, voffV[j]);
     }
   };
 
-  fetch(t_begin, 0);
-  if (t_begin + 1 < t_end) fetch(t_begin + 1, 1);
-
-  u32x4 qf[NQB][DQK];
-  int qpos[NQB];
-  bool rok[NQB];
-  size_t roff[NQB];
+  uint16_t* const sk = smem;
+  uint16_t* const sv = smem + kPipeVRegion;
+  fetch(t_begin, sk, sv);
+  if (t_begin + 1 < t_end) fetch(t_begin + 1, sk + TILE, sv + TILE);
+  if (t_begin + 2 < t_end) fetch(t_begin + 2, sk + 2 * TILE, sv + 2 * TILE);
+  // Stage 3's V tile stands in for "the tile before the first" (with zero
+  // probabilities): clear it so that it holds finite values.
+  {
+    uint16_t* z = sv + 3 * TILE;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int r = (wave * NQB + qb) * 16 + c16;
-    const int pl = r / G, hr = r % G;
-    rok[qb] = pl < m_eff;
-    const int pos = q0 + pl;
-    qpos[qb] = pos + off;
-    const int head = kvh * G + hr;
-    roff[qb] = (((size_t)b * a.Hq + head) * a.Lq + (rok[qb] ? pos : 0)) * D;
-    load_q<DQK>(qf[qb], qg + roff[qb], rok[qb], D, g4);
+    for (int i = 0; i < TILE / (8 * 512); ++i)
+      *reinterpret_cast<u32x4*>(z + (i * 512 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
   }
 
-  float m_e[NQB], l_p[NQB];
-  f32x4 o[NQB][DV];
+  PipeAddr ad;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m_e[qb] = kNegInf;
-    l_p[qb] = 0.f;
+  for (int t = 0; t < 4; ++t) ad.ka[t] = c16 * 128 + (((4 * t + g4) ^ c16) << 3);
+  {
+    const int row = 4 * g4 + (c16 >> 2);
+    const int sw = 2 * (row & 7);
 #pragma unroll
-    for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 8; ++db)
+      ad.va[db] = row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1);
   }
 
-  int sc = 0;  // LDS stage of tile t
-  for (int t = t_begin; t < t_end; ++t) {
-    // This wave's loads of tile t are done once at most the next tile's
-    // 2*IPW loads are still outstanding; the barrier publishes every wave's.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (t + 1 < t_end) {
-      if constexpr (IPW == 2)
-        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (t_begin + 2 < t_end)
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tiles t_begin+1, +2 may still fly
+  else if (t_begin + 1 < t_end)
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+
+  float m_e[2] = {kNegInf, kNegInf};
+  f32x4 o[2][8], ls[2];
+  f32x4 sa[2][2], sb[2][2];
+  u32x4 pa[2], pb[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pb[qb] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Scores of the first step (stage 0, tile rows 0..31).
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc = Elem<T>::mfma(*reinterpret_cast<const u32x4*>(sk + ad.ka[t] + hh * 16 * 128), qf[qb][t], acc);
+      sa[qb][hh] = acc;
     }
+
+  auto step_full = [&](int kg0) {
+    bool full = kg0 + 32 <= a.Lkv;
+    if (a.causal) full = full && (kg0 + 31 <= pos_min);
+    if (a.window > 0) {
+      full = full && (pos_max - kg0 < a.window);
+      if (!a.causal) full = full && (kg0 + 31 - pos_min < a.window);
+    }
+    return full;
+  };
+  // Tile t in stage ST (compile time).  First half: softmax of keys
+  // [64t, 64t+32), scores of [64t+32, 64t+64), P.V of the previous tile's
+  // second half (stage ST-1).  Second half: softmax of [64t+32, 64t+64),
+  // scores of the next tile's first half (stage ST+1; discarded after the
+  // last tile), P.V of this tile's first half.
+  auto tile = [&](auto stc, int t) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int SP = (ST + kPipeStages - 1) % kPipeStages, SN = (ST + 1) % kPipeStages;
+    {
+      const int kg0 = t * KEYS;
+      const int ub[2] = {kg0 + rconst[0], kg0 + rconst[1]};
+      pipe_step<T, SOFTCAP, FIXREF, ST * TILE + 32 * 128, SP * TILE + 32 * 128>(!step_full(kg0), sk, sv, ad, sa, sb, pb,
+                                                                                pa, qf, o, ls, m_e, ub, span, a);
+    }
+    // Tile t+1 must be in LDS, and every wave past the first half (so done
+    // with tile t-1, whose stage now takes tile t+3).
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (t + 2 < t_end)
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): tile t+2 may still fly
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    // Every wave is past tile t-1, so its stage takes tile t+2.
-    if (t + 2 < t_end) fetch(t + 2, sc == 0 ? 2 : sc - 1);
-    const int k0 = t * KEYS;
-    const uint16_t* Ks = smem + sc * STAGE;
-    const uint16_t* Vs = Ks + TILE;
-    bool full = k0 + KEYS <= a.Lkv;
-    if (a.causal) full = full && (k0 + KEYS - 1 <= pos_min);
-    if (a.window > 0) {
-      full = full && (pos_max - k0 < a.window);
-      if (!a.causal) full = full && (k0 + KEYS - 1 - pos_min < a.window);
+    if (t + 3 < t_end) fetch(t + 3, sk + SP * TILE, sv + SP * TILE);
+    {
+      const int kg0 = t * KEYS + 32;
+      const int ub[2] = {kg0 + rconst[0], kg0 + rconst[1]};
+      pipe_step<T, SOFTCAP, FIXREF, SN * TILE, ST * TILE>(!step_full(kg0), sk, sv, ad, sb, sa, pa, pb, qf, o, ls, m_e,
+                                                          ub, span, a);
     }
-    tile_pair<T, DQK, DV, NQB, 0, 0, true, SOFTCAP, MGQA_EARLY_FRAG>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16, g4);
-    sc = (sc == 2) ? 0 : sc + 1;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  int t = t_begin, last = 0;
+  while (true) {
+    tile(S0{}, t);
+    if (++t >= t_end) { last = 0; break; }
+    tile(S1{}, t);
+    if (++t >= t_end) { last = 1; break; }
+    tile(S2{}, t);
+    if (++t >= t_end) { last = 2; break; }
+    tile(S3{}, t);
+    if (++t >= t_end) { last = 3; break; }
+  }
+  // P.V and row sums of the last step (second half of the last tile).
+  {
+    const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
+                        OnesOperand<T>::kPair};
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint16_t* v0 = sv + ad.va[db] + last * TILE + 32 * 128;
+      const u32x2 lo = lds_read_tr4(v0);
+      const u32x2 hi = lds_read_tr4(v0 + 16 * 128);
+      const u32x4 v1 = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[qb][db] = Elem<T>::mfma(v1, pb[qb], o[qb][db]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) ls[qb] = Elem<T>::mfma(ones, pb[qb], ls[qb]);
   }
 
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float l = col_sum(l_p[qb]);
-    if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, D, g4);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = (wave * 2 + qb) * 16 + c16;
+    const int pl = r / G, hr = r % G;
+    if (pl < m_eff) {
+      const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + q0 + pl) * D;
+      store_row<T, 8>(og + ro, o[qb], 1.0f / ls[qb][0], D, g4);
+    }
   }
 }
 
@@ -1082,7 +1380,15 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
       default: return hipErrorInvalidValue;
     }
   } else if (args.d == 128) {
-    hipLaunchKernelGGL((prefill128_kernel<T, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
+    // Fixed softmax reference: bf16 probabilities and a softcap small enough
+    // that every exponent stays in range (c * log2(e) <= 83).
+    if constexpr (SOFTCAP && __is_same(T, __bf16)) {
+      if (args.c2 <= 83.0f) {
+        hipLaunchKernelGGL((prefill_pipe_kernel<T, true, true>), grid, dim3(512), 0, st, args);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((prefill_pipe_kernel<T, SOFTCAP, false>), grid, dim3(512), 0, st, args);
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   }
