@@ -69,15 +69,18 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   const long long rows_all = (long long)G * Lq;
   const int max_nqb = p.dv <= kSplitWideMaxDv ? kSplitMaxNqb : kSplitMaxNqbWide;
 
-  // Prefill kernel: its 256-row block, when that still gives a workgroup per CU.
-  const int m_big = 16 * kPrefillWaves * kPrefillNqb / G;
+  // Prefill kernels: 256-row blocks (128-row blocks, two workgroups per CU,
+  // for head size 128), when that still gives a workgroup per CU.
+  const bool d128 = (d == 128);
+  const int rows_big = d128 ? 16 * kPipe4Waves * kPrefillNqb : 16 * kPrefillWaves * kPrefillNqb;
+  const int m_big = rows_big / G;
   const long long wgs_big = units * ((Lq + m_big - 1) / m_big);
   if (rows_all > 16LL * max_nqb && wgs_big >= kCUs) {
     p.path = kPathPrefill;
-    p.keys_per_tile = kPrefillKeys;
+    p.keys_per_tile = d128 ? kPipe4Keys : kPrefillKeys;
     p.nsplit = 1;
     p.nqb = kPrefillNqb;
-    p.nwaves = kPrefillWaves;
+    p.nwaves = d128 ? kPipe4Waves : kPrefillWaves;
     p.rows_per_wg = 16 * p.nwaves * p.nqb;
     p.m = m_big;
     p.n_pos_blk = (Lq + m_big - 1) / m_big;

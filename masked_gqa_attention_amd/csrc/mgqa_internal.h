@@ -12,6 +12,9 @@ namespace mgqa {
 constexpr int kPrefillKeys = 64;
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillNqb = 2;
+// Head size 128: four waves x 2 blocks of 16 rows, 32-key tiles.
+constexpr int kPipe4Waves = 4;
+constexpr int kPipe4Keys = 32;
 // Split-KV kernel: waves per workgroup; each wave takes 32 keys of a tile.
 #ifndef MGQA_SPLIT_WAVES
 #define MGQA_SPLIT_WAVES 4

@@ -1093,6 +1093,252 @@ __global__ __launch_bounds__(512) void prefill_pipe_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The same pipelined steps with four waves (one per SIMD) and 128 rows per
+// workgroup, one 32-key tile per step, five LDS stages of 16 KB: two
+// workgroups fit in one CU's LDS, so every SIMD runs waves of two
+// independent workgroups, whose barriers and load waits do not line up.
+// Tile j+3 is requested once every wave is past step j-1 (the last reader
+// of tile j-2's stage), two steps before it is first read.
+// ---------------------------------------------------------------------------
+constexpr int kPipe4Stages = 5;
+constexpr int kPipe4Tile = 32 * 128;                       // elements of one K or V tile
+constexpr int kPipe4VRegion = kPipe4Stages * kPipe4Tile;  // first V tile (elements)
+
+template <typename T, bool SOFTCAP, bool FIXREF>
+__global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
+  constexpr int NWAVES = 4, D = 128, KEYS = 32, TILE = kPipe4Tile, NS = kPipe4Stages;
+  constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row direct-to-LDS loads per wave per tensor
+  static_assert(IPW == 2, "the wait counts below assume two loads per tensor per wave");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NS * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int g4 = lane >> 4, c16 = lane & 15;
+
+  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
+  // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
+  // range of (unit, position block) pairs: the blocks of one unit then share
+  // their K/V tiles in one L2.
+  const int bid = blockIdx.x;
+  int lin = bid;
+  if ((gridDim.x & 7) == 0) lin = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+  const int pblk = lin % a.n_pos_blk;
+  const int unit = lin / a.n_pos_blk;  // b * Hkv + kvh
+  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int G = a.G;
+  const int q0 = pblk * a.m;
+  const int m_eff = min(a.m, a.Lq - q0);
+  const int off = a.Lkv - a.Lq;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
+  uint16_t* og = static_cast<uint16_t*>(a.out);
+
+  // Key band of this block of positions, in tiles.
+  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
+  int key_lo = 0, key_hi = a.Lkv - 1;
+  if (a.causal) key_hi = min(key_hi, pos_max);
+  if (a.window > 0) {
+    key_lo = max(0, pos_min - a.window + 1);
+    if (!a.causal) key_hi = min(key_hi, pos_max + a.window - 1);
+  }
+  const int t_begin = key_lo / KEYS, t_end = key_hi / KEYS + 1;
+
+  // Q first: the direct-to-LDS loads are counted after it, so waiting for
+  // the first tile also waits for Q.
+  u32x4 qf[2][4];
+  int rconst[2], span[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = (wave * 2 + qb) * 16 + c16;
+    const int pl = r / G, hr = r % G;
+    const bool ok = pl < m_eff;
+    const int pos = q0 + pl + off;
+    const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (ok ? q0 + pl : 0)) * D;
+    load_q<4>(qf[qb], qg + ro, ok, D, g4);
+    // Visible keys of this row: [lo, hi].
+    const int lo = a.window > 0 ? pos - a.window + 1 : 0;
+    int hi = a.Lkv - 1;
+    if (a.causal) hi = min(hi, pos);
+    else if (a.window > 0) hi = min(hi, pos + a.window - 1);
+    rconst[qb] = 4 * g4 - lo;
+    span[qb] = hi - lo;
+  }
+
+  int voffK[IPW], voffV[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int row = 4 * (wave * IPW + j) + (lane >> 4), slot = lane & 15;
+    voffK[j] = (row * D + ((slot ^ (row & 15)) << 3)) * 2;
+    voffV[j] = (row * D + ((slot ^ (2 * (row & 7))) << 3)) * 2;
+  }
+  uint16_t* const sk = smem;
+  uint16_t* const sv = smem + kPipe4VRegion;
+  auto fetch = [&](int t, int st) {
+    // (Forced into scalar registers: the descriptor must be uniform.)
+    const int k0 = wave_uniform(t * KEYS);
+    const uint32_t bytes = (uint32_t)wave_uniform((a.Lkv - k0) * (D * 2));
+    const u32x4 rk = raw_rsrc(kg + (size_t)k0 * D, bytes);
+    const u32x4 rv = raw_rsrc(vg + (size_t)k0 * D, bytes);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int row0 = st * TILE + (wave * IPW + j) * 4 * D;
+      lds_dma16_async(rk, sk + row0, voffK[j]);
+      lds_dma16_async(rv, sv + row0, voffV[j]);
+    }
+  };
+
+  // Tiles t_begin .. t_begin+2 into stages 0..2.
+  fetch(t_begin, 0);
+  if (t_begin + 1 < t_end) fetch(t_begin + 1, 1);
+  if (t_begin + 2 < t_end) fetch(t_begin + 2, 2);
+  // The last stage's V tile stands in for "the tile before the first" (with
+  // zero probabilities): clear it so that it holds finite values.
+  {
+    uint16_t* z = sv + (NS - 1) * TILE;
+#pragma unroll
+    for (int i = 0; i < TILE / (8 * 256); ++i)
+      *reinterpret_cast<u32x4*>(z + (i * 256 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  PipeAddr ad;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) ad.ka[t] = c16 * 128 + (((4 * t + g4) ^ c16) << 3);
+  {
+    const int row = 4 * g4 + (c16 >> 2);
+    const int sw = 2 * (row & 7);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      ad.va[db] = row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1);
+  }
+
+  // Tiles t_begin and t_begin+1 in LDS (t_begin+2 may still fly).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (t_begin + 2 < t_end)
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+
+  float m_e[2] = {kNegInf, kNegInf};
+  f32x4 o[2][8], ls[2];
+  f32x4 sa[2][2], sb[2][2];
+  u32x4 pa[2], pb[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pb[qb] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Scores of the first step (stage 0).
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc = Elem<T>::mfma(*reinterpret_cast<const u32x4*>(sk + ad.ka[t] + hh * 16 * 128), qf[qb][t], acc);
+      sa[qb][hh] = acc;
+    }
+
+  auto step_full = [&](int kg0) {
+    bool full = kg0 + KEYS <= a.Lkv;
+    if (a.causal) full = full && (kg0 + KEYS - 1 <= pos_min);
+    if (a.window > 0) {
+      full = full && (pos_max - kg0 < a.window);
+      if (!a.causal) full = full && (kg0 + KEYS - 1 - pos_min < a.window);
+    }
+    return full;
+  };
+  // Step t (tile t in stage ST, compile time): softmax of tile t, scores of
+  // tile t+1 (stage ST+1; discarded after the last tile), P.V of tile t-1
+  // (stage ST-1).  Before it: tile t+1 landed, and every wave past step t-1.
+  // sc/sn/pp/pc alternate between the two register sets from step to step.
+  auto step = [&](auto stc, int t, f32x4 (&sc)[2][2], f32x4 (&sn)[2][2], const u32x4 (&pp)[2], u32x4 (&pc)[2]) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int SP = (ST + NS - 1) % NS, SN = (ST + 1) % NS;
+    if (t > t_begin) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (t + 2 < t_end)
+        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): tile t+2 may still fly
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __syncthreads();
+    }
+    // Tile t-2's stage is free: every wave is past step t-1, its last reader.
+    if (t + 3 < t_end) fetch(t + 3, (ST + 3) % NS);
+    const int kg0 = t * KEYS;
+    const int ub[2] = {kg0 + rconst[0], kg0 + rconst[1]};
+    pipe_step<T, SOFTCAP, FIXREF, SN * TILE, SP * TILE>(!step_full(kg0), sk, sv, ad, sc, sn, pp, pc, qf, o, ls, m_e,
+                                                        ub, span, a);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using S4 = std::integral_constant<int, 4>;
+  // Ten steps per turn: five stages, two register sets.
+  int t = t_begin, last = 0;
+  while (true) {
+    step(S0{}, t, sa, sb, pb, pa);
+    if (++t >= t_end) { last = 0; break; }
+    step(S1{}, t, sb, sa, pa, pb);
+    if (++t >= t_end) { last = 1; break; }
+    step(S2{}, t, sa, sb, pb, pa);
+    if (++t >= t_end) { last = 2; break; }
+    step(S3{}, t, sb, sa, pa, pb);
+    if (++t >= t_end) { last = 3; break; }
+    step(S4{}, t, sa, sb, pb, pa);
+    if (++t >= t_end) { last = 4; break; }
+    step(S0{}, t, sb, sa, pa, pb);
+    if (++t >= t_end) { last = 5; break; }
+    step(S1{}, t, sa, sb, pb, pa);
+    if (++t >= t_end) { last = 6; break; }
+    step(S2{}, t, sb, sa, pa, pb);
+    if (++t >= t_end) { last = 7; break; }
+    step(S3{}, t, sa, sb, pb, pa);
+    if (++t >= t_end) { last = 8; break; }
+    step(S4{}, t, sb, sa, pa, pb);
+    if (++t >= t_end) { last = 9; break; }
+  }
+  // P.V and row sums of the last tile (its probabilities are in pa after an
+  // even-numbered step of the turn, in pb after an odd one).
+  {
+    const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
+                        OnesOperand<T>::kPair};
+    const u32x4* pl = (last & 1) ? pb : pa;
+    u32x4 pfin[2] = {pl[0], pl[1]};
+    const int vst = (last % NS) * TILE;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint16_t* v0 = sv + ad.va[db] + vst;
+      const u32x2 lo = lds_read_tr4(v0);
+      const u32x2 hi = lds_read_tr4(v0 + 16 * 128);
+      const u32x4 v1 = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[qb][db] = Elem<T>::mfma(v1, pfin[qb], o[qb][db]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) ls[qb] = Elem<T>::mfma(ones, pfin[qb], ls[qb]);
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = (wave * 2 + qb) * 16 + c16;
+    const int pl = r / G, hr = r % G;
+    if (pl < m_eff) {
+      const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + q0 + pl) * D;
+      store_row<T, 8>(og + ro, o[qb], 1.0f / ls[qb][0], D, g4);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Split-KV kernel (decode, multi-token decode, short and mid-length
 // sequences): one workgroup of NW waves per (unit = batch*Hkv + kv head, block
 // of m query positions, key split).  Its rows are (position, head of the group)
@@ -1384,11 +1630,11 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
     // that every exponent stays in range (c * log2(e) <= 83).
     if constexpr (SOFTCAP && __is_same(T, __bf16)) {
       if (args.c2 <= 83.0f) {
-        hipLaunchKernelGGL((prefill_pipe_kernel<T, true, true>), grid, dim3(512), 0, st, args);
+        hipLaunchKernelGGL((prefill_pipe4_kernel<T, true, true>), grid, dim3(64 * kPipe4Waves), 0, st, args);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((prefill_pipe_kernel<T, SOFTCAP, false>), grid, dim3(512), 0, st, args);
+    hipLaunchKernelGGL((prefill_pipe4_kernel<T, SOFTCAP, false>), grid, dim3(64 * kPipe4Waves), 0, st, args);
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
   }
