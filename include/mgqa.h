@@ -126,8 +126,9 @@ int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const floa
                     int* length_out, void* stream);
 
 /* Plan the library would use for this shape, without touching the GPU.
- * info[0] path: 0 = prefill kernel (256-row workgroups, every wave sweeps the
- *         whole key band), 1 = split-KV kernel (decode, multi-token decode and
+ * info[0] path: 0 = prefill kernel (every wave sweeps the whole key band of
+ *         its rows; 128-row workgroups for head size 128, 256-row otherwise),
+ *         1 = split-KV kernel (decode, multi-token decode and
  *         short sequences: the waves of a workgroup, and possibly several
  *         workgroups, split the key band of its rows)
  * info[1] workgroups launched
