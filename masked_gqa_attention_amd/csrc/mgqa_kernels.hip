@@ -1360,18 +1360,24 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int OP = DVP + 4;  // LDS pitch of the merged wave outputs (floats)
   // K and V tiles; after the key loop the same bytes hold one row block's wave outputs.
   constexpr int TILE_BYTES = KEYS * (KP + VP) * 2;
-  constexpr int MERGE_BYTES = NW * 16 * OP * 4;
+  constexpr int MERGE_BYTES = NW * NQB * 16 * OP * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vs = Ks + KEYS * KP;
-  float (*wo)[16 * OP] = reinterpret_cast<float (*)[16 * OP]>(smem);
-  __shared__ float wm[NW][16], wl[NW][16];
+  float (*wo)[NQB * 16 * OP] = reinterpret_cast<float (*)[NQB * 16 * OP]>(smem);
+  __shared__ float wm[NW][NQB * 16], wl[NW][NQB * 16];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int split = blockIdx.x % a.nsplit;
-  const int grp = blockIdx.x / a.nsplit;  // unit * n_pos_blk + position block
+  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
+  // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
+  // range of (group, split) pairs: the position blocks of one unit, which
+  // read the same K/V rows, then share them in one L2.
+  int lin = blockIdx.x;
+  if ((gridDim.x & 7) == 0) lin = (lin & 7) * (int)(gridDim.x >> 3) + (lin >> 3);
+  const int split = lin % a.nsplit;
+  const int grp = lin / a.nsplit;  // unit * n_pos_blk + position block
   const int pblk = grp % a.n_pos_blk;
   const int unit = grp / a.n_pos_blk;
   const int kvh = unit % a.Hkv, b = unit / a.Hkv;
@@ -1467,63 +1473,61 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
           Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
   }
 
-  // ---- merge the wave states (fixed order), one 16-row block at a time --------
-  // Thread -> float4 chunks q = tid + NT*j of a [16][DVP] block: row q / CPR,
-  // columns 4*(q % CPR) .. +3, so a wave touches contiguous memory.
+  // ---- merge the wave states (fixed order) ------------------------------------
+  // Every wave writes its (max, sum, unnormalised rows) of all row blocks to
+  // LDS with 16-byte stores; after one barrier, thread -> float4 chunks
+  // q = tid + NT*j of the [rows][DVP] output: row q / CPR, columns
+  // 4*(q % CPR) .. +3, so a wave touches contiguous memory.
   constexpr int CPR = DVP / 4;
-  constexpr int JN = (16 * CPR + NT - 1) / NT;
+  constexpr int JN = (NQB * 16 * CPR + NT - 1) / NT;
   const int rstride = a.nrows;  // rows of a full block: partial layout stride
   const int pidx = (grp * a.nsplit + split) * rstride;
   const uint32_t o_bytes = (uint32_t)gridDim.x * rstride * DVP * 4;
   const uint32_t ml_bytes = (uint32_t)gridDim.x * rstride * 8;
   const auto rs_o = make_rsrc(a.ws_o, o_bytes);
   const auto rs_ml = make_rsrc(a.ws_ml, ml_bytes);
+  __syncthreads();  // the tiles are no longer read
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    if (16 * qb >= nrows) break;
-    __syncthreads();  // tiles (or the previous block's outputs) are no longer read
     const float l = col_sum(l_p[qb]);
     if (g4 == 0) {
-      wm[wave][c16] = m_e[qb];
-      wl[wave][c16] = l;
+      wm[wave][16 * qb + c16] = m_e[qb];
+      wl[wave][16 * qb + c16] = l;
     }
 #pragma unroll
     for (int db = 0; db < DV; ++db)
+      *reinterpret_cast<f32x4*>(&wo[wave][(16 * qb + c16) * OP + 16 * db + 4 * g4]) = o[qb][db];
+  }
+  __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wo[wave][c16 * OP + 16 * db + 4 * g4 + i] = o[qb][db][i];
-    __syncthreads();
-
+  for (int j = 0; j < JN; ++j) {
+    const int q = tid + j * NT;
+    const int r = q / CPR, c4 = q % CPR;
+    if (q >= NQB * 16 * CPR || r >= nrows) continue;
+    float M = kNegInf, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < JN; ++j) {
-      const int q = tid + j * NT;
-      const int row = min(q / CPR, 15), c4 = q % CPR;
-      const int r = 16 * qb + row;
-      if (q >= 16 * CPR || r >= nrows) continue;
-      float M = kNegInf, L = 0.f;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][r]);
+    if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][row]);
-      if (M != kNegInf) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float f = fast_exp2(wm[w][row] - M);
-          L += f * wl[w][row];
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&wo[w][row * OP + 4 * c4]);
-          acc += f * x;
-        }
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(wm[w][r] - M);
+        L += f * wl[w][r];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&wo[w][r * OP + 4 * c4]);
+        acc += f * x;
       }
-      if (a.nsplit == 1) {
-        if (4 * c4 < d) {
-          const float inv = 1.0f / L;
-          const size_t oo = (((size_t)b * a.Hq + kvh * G + r % G) * a.Lq + q0 + r / G) * d + 4 * c4;
-          *reinterpret_cast<u32x2*>(og + oo) =
-              u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
-        }
-      } else {
-        // This split's partial, with device-coherent stores.
-        st_dev16(rs_o, ((pidx + r) * DVP + 4 * c4) * 4, acc);
-        if (c4 == 0) st_dev8(rs_ml, (pidx + r) * 8, f32x2{M, L});
+    }
+    if (a.nsplit == 1) {
+      if (4 * c4 < d) {
+        const float inv = 1.0f / L;
+        const size_t oo = (((size_t)b * a.Hq + kvh * G + r % G) * a.Lq + q0 + r / G) * d + 4 * c4;
+        *reinterpret_cast<u32x2*>(og + oo) =
+            u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
       }
+    } else {
+      // This split's partial, with device-coherent stores.
+      st_dev16(rs_o, ((pidx + r) * DVP + 4 * c4) * 4, acc);
+      if (c4 == 0) st_dev8(rs_ml, (pidx + r) * 8, f32x2{M, L});
     }
   }
   if (a.nsplit == 1) return;
