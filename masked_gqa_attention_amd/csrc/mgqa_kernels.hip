@@ -1414,9 +1414,17 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     if (RING) vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
     else vt.load(vg, k0, a.Lkv, d);
   };
-  if (t0 < t1) {
-    fetch_k(t0 * KEYS);
-    fetch_v(t0 * KEYS);
+  // The tiles of the range are visited in a rotated order that differs from
+  // workgroup to workgroup, so that the workgroups do not all start on
+  // addresses with the same alignment (which concentrates the first requests
+  // on a few memory channels).  The softmax merge is order independent; the
+  // order is a fixed function of the shape, so results stay reproducible.
+  const int ntile = max(t1 - t0, 0);
+  const int rot = ntile > 0 ? (int)(((unsigned)lin * 5u) % (unsigned)ntile) : 0;
+  auto tile_at = [&](int i) { const int r = i + rot; return t0 + (r >= ntile ? r - ntile : r); };
+  if (ntile > 0) {
+    fetch_k(tile_at(0) * KEYS);
+    fetch_v(tile_at(0) * KEYS);
   }
 
   // This lane's rows: column c16 of each 16-row block.
@@ -1443,17 +1451,19 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   }
 
   u32x4 kf_unused[2][DQK];
-  for (int t = t0; t < t1; ++t) {
+  for (int it = 0; it < ntile; ++it) {
+    const int t = tile_at(it);
     const int k0 = t * KEYS;
     __syncthreads();  // every wave is done with the previous tile
     // Each half of the staging registers is refilled with the next tile as
     // soon as it is in LDS, so loads stay in flight while the other half is
     // written, and the next tile flies during this one.
-    const bool more = t + 1 < t1;
+    const bool more = it + 1 < ntile;
+    const int kn = more ? tile_at(it + 1) * KEYS : 0;
     kt.store(Ks, tid);
-    if (more) fetch_k(k0 + KEYS);
+    if (more) fetch_k(kn);
     vt.store(Vs, tid);
-    if (more) fetch_v(k0 + KEYS);
+    if (more) fetch_v(kn);
     __syncthreads();
     // This wave's 32 keys: skipped when wholly outside the band, unmasked
     // when wholly inside it.
