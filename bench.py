@@ -134,6 +134,13 @@ def figures(w, ms):
             "frac": tf / MFMA_PEAK_TFLOPS, "alg_bytes": wk["bytes"], "alg_flops": wk["flops"]}
 
 
+def kernel_name(plan, w) -> str:
+    """The attention kernel a plan launches (as in the library's dispatch)."""
+    if plan.get("path") == 1:
+        return "splitkv_kernel"
+    return "prefill_pipe4_kernel" if w.d == 128 else "prefill_kernel"
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -239,7 +246,7 @@ def main(argv=None) -> int:
         rc, plan = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
                                   w.softcap, 0 if w.dtype == "bf16" else 1)
         results[name] = {"ms": ms, "steps": steps, "copies": copies, **fig,
-                         "kernel": "splitkv_kernel" if plan.get("path") == 1 else "prefill_kernel",
+                         "kernel": kernel_name(plan, w),
                          "plan": plan, "shape": w.describe()}
         log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
             f"({100 * fig['frac']:.1f}% of {fig['bound']} peak)")
