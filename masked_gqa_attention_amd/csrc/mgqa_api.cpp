@@ -16,11 +16,9 @@ namespace {
 constexpr int kCUs = 256;              // MI355X compute units
 // Split-KV path: position blocks and key splits are chosen so that about this
 // many workgroups run.
-#ifndef MGQA_SPLIT_TARGET_WGS
-#define MGQA_SPLIT_TARGET_WGS 256
-#endif
-constexpr long long kSplitTarget = MGQA_SPLIT_TARGET_WGS;
-constexpr int kMaxCounters = kSplitTarget > 256 ? (int)kSplitTarget : 256;  // leading counter block
+constexpr long long kSplitTarget = 256;
+constexpr int kMaxCounters = 256;  // leading counter block
+static_assert(kSplitTarget <= kMaxCounters, "split plans need one counter per group");
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

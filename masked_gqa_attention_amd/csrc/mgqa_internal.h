@@ -16,15 +16,9 @@ constexpr int kPrefillNqb = 2;
 constexpr int kPipe4Waves = 4;
 constexpr int kPipe4Keys = 32;
 // Split-KV kernel: waves per workgroup; each wave takes 32 keys of a tile.
-#ifndef MGQA_SPLIT_WAVES
-#define MGQA_SPLIT_WAVES 4
-#endif
-constexpr int kSplitWaves = MGQA_SPLIT_WAVES;
+constexpr int kSplitWaves = 4;
 constexpr int kSplitKeys = 32 * kSplitWaves;
-#ifndef MGQA_SPLIT_MAX_NQB
-#define MGQA_SPLIT_MAX_NQB 4
-#endif
-constexpr int kSplitMaxNqb = MGQA_SPLIT_MAX_NQB;  // 16-row blocks per workgroup, head size <= 96
+constexpr int kSplitMaxNqb = 4;     // 16-row blocks per workgroup, head size <= 96
 constexpr int kSplitMaxNqbWide = 2; // head size > 96 (register budget)
 constexpr int kSplitWideMaxDv = 6;  // P.V 16-column blocks up to which 3 and 4 row blocks exist
 

@@ -323,116 +323,34 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Prefill per-wave tile work.  A step is 32 keys: S^T blocks hh = 0, 1 of 16
-// keys each, natural key order (block row rho is key kbase + 16*hh + rho), so
-// lane group g4 holds keys 4*g4 + i (hh = 0) and 16 + 4*g4 + i (hh = 1): the
-// P^T operand that the transposed V reads above produce.  LDS fragments are
-// read one phase ahead of their use -- V for the step before the softmax
-// arithmetic, K for the next step before the P.V products -- so LDS latency
-// overlaps other work.
+// Per-wave tile work of the register-staged kernels (prefill_kernel,
+// splitkv_kernel).  A step is 32 keys: S^T blocks hh = 0, 1 of 16 keys each,
+// natural key order (block row rho is key kbase + 16*hh + rho), so lane group
+// g4 holds keys 4*g4 + i (hh = 0) and 16 + 4*g4 + i (hh = 1): the P^T operand
+// that the transposed V reads above produce.  K and V rows are padded to KP /
+// VP elements in LDS, which puts the rows of one fragment read on distinct
+// banks.
 
-// Two LDS tile layouts.  Padded (SWZ = false): rows of KP / VP elements, the
-// padding puts the rows of one read on distinct banks.  Swizzled (SWZ = true,
-// head size 128 only): dense 256-byte rows of sixteen 16-byte slots; chunk c
-// of K row r sits in slot c ^ (r % 16) and chunk c of V row r in slot
-// c ^ 2*(r % 8), which keeps a K-fragment read (16 rows, one chunk) and a
-// transposed V read (4 rows x 2 chunks per 16 lanes) on distinct banks and
-// lets whole rows be written by direct global-to-LDS loads.
-template <int DQK, int KP, bool SWZ>
-__device__ __forceinline__ void read_kfrag(u32x4 (&kf)[2][DQK], const uint16_t* Ks, int kbase, int c16,
-                                           int g4) {
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int row = kbase + 16 * hh + c16;  // row % 16 == c16
-#pragma unroll
-    for (int t = 0; t < DQK; ++t) {
-      const uint16_t* p = SWZ ? Ks + row * 128 + (((4 * t + g4) ^ c16) << 3) : Ks + row * KP + 8 * g4 + 32 * t;
-      kf[hh][t] = *reinterpret_cast<const u32x4*>(p);
-    }
-  }
-}
-
-template <int DV, int VP, bool SWZ>
-__device__ __forceinline__ void read_vfrag(u32x4 (&vf)[DV], const uint16_t* Vs, int kbase, int c16,
-                                           int g4) {
-  const int row = kbase + 4 * g4 + (c16 >> 2);
-  const int sw = 2 * ((4 * (g4 & 1) + (c16 >> 2)) & 7);  // 2 * (row % 8)
-#pragma unroll
-  for (int db = 0; db < DV; ++db) {
-    const uint16_t* v0;
-    if (SWZ)
-      v0 = Vs + row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1);
-    else
-      v0 = Vs + row * VP + 4 * (c16 & 3) + 16 * db;
-    const uint16_t* v1 = v0 + 16 * (SWZ ? 128 : VP);
-    const u32x2 lo = lds_read_tr4(v0);
-    const u32x2 hi = lds_read_tr4(v1);
-    vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-  }
-}
-
-// One 32-key step: scores from kf, softcap/mask/online softmax, P.V from V
-// fragments read here.  When NEXT_K, kf is refilled with the fragments of the
-// step at tile-local key kbase + 32 before the P.V products.
-template <int KP, bool SWZ>
-__device__ __forceinline__ u32x4 read_kfrag1(const uint16_t* Ks, int kbase, int hh, int t, int c16,
-                                             int g4) {
-  const int row = kbase + 16 * hh + c16;
-  const uint16_t* p = SWZ ? Ks + row * 128 + (((4 * t + g4) ^ c16) << 3) : Ks + row * KP + 8 * g4 + 32 * t;
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-template <int VP, bool SWZ>
-__device__ __forceinline__ u32x4 read_vfrag1(const uint16_t* Vs, int kbase, int db, int c16, int g4) {
-  const int row = kbase + 4 * g4 + (c16 >> 2);
-  const int sw = 2 * ((4 * (g4 & 1) + (c16 >> 2)) & 7);  // 2 * (row % 8)
-  const uint16_t* v0 = SWZ ? Vs + row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1)
-                           : Vs + row * VP + 4 * (c16 & 3) + 16 * db;
-  const uint16_t* v1 = v0 + 16 * (SWZ ? 128 : VP);
-  const u32x2 lo = lds_read_tr4(v0);
-  const u32x2 hi = lds_read_tr4(v1);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
-template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SWZ, bool SOFTCAP, bool MASK,
-          bool NEXT_K, bool EARLY>
+// One 32-key step: scores, softcap, mask, online softmax and P.V; each
+// fragment is read from LDS right before its products.
+template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SOFTCAP, bool MASK>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int kbase, int kglob0,
-                                          u32x4 (&kf)[2][DQK], const u32x4 (&qf)[NQB][DQK],
-                                          const int (&qpos)[NQB], float (&m_e)[NQB],
-                                          float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                          const u32x4 (&qf)[NQB][DQK], const int (&qpos)[NQB],
+                                          float (&m_e)[NQB], float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
                                           const KernelArgs& a, int c16, int g4) {
   // ---- S^T = K Q^T -------------------------------------------------------
   f32x4 s[NQB][2];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (EARLY) {
 #pragma unroll
-    for (int t = 0; t < DQK; ++t)
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint16_t* krow = Ks + (kbase + 16 * hh + c16) * KP;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+    for (int t = 0; t < DQK; ++t) {
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(krow + 8 * g4 + 32 * t);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][hh] = Elem<T>::mfma(kf[hh][t], qf[qb][t], s[qb][hh]);
-    __builtin_amdgcn_sched_barrier(0);
-  } else {
-    // One fragment at a time: read, then its NQB products.
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint16_t* krow = Ks + (kbase + 16 * hh + c16) * (SWZ ? 128 : KP);
-#pragma unroll
-      for (int t = 0; t < DQK; ++t) {
-        const uint16_t* p = SWZ ? krow + (((4 * t + g4) ^ c16) << 3) : krow + 8 * g4 + 32 * t;
-        const u32x4 k1 = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][hh] = Elem<T>::mfma(k1, qf[qb][t], s[qb][hh]);
-      }
+      for (int qb = 0; qb < NQB; ++qb) s[qb][hh] = Elem<T>::mfma(k1, qf[qb][t], s[qb][hh]);
     }
-  }
-
-  // ---- V fragments for this step (early: in flight during the softmax) ------
-  u32x4 vf[DV];
-  if (EARLY) {
-    read_vfrag<DV, VP, SWZ>(vf, Vs, kbase, c16, g4);
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- softcap, mask, online softmax, P^T ------------------------------------
@@ -493,68 +411,32 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
     pk[qb] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
                    Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
   }
-  if (EARLY) __builtin_amdgcn_sched_barrier(0);
 
-  // ---- (early: next step's K fragments), then O^T += V^T P^T -----------------
-  if (EARLY) {
-    if (NEXT_K) read_kfrag<DQK, KP, SWZ>(kf, Ks, kbase + 32, c16, g4);
+  // ---- O^T += V^T P^T ---------------------------------------------------------
+  const uint16_t* v0 = Vs + (kbase + 4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3);
+  const uint16_t* v1 = v0 + 16 * VP;
 #pragma unroll
-    for (int db = 0; db < DV; ++db)
+  for (int db = 0; db < DV; ++db) {
+    const u32x2 lo = lds_read_tr4(v0 + 16 * db);
+    const u32x2 hi = lds_read_tr4(v1 + 16 * db);
+    const u32x4 vf1 = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf[db], pk[qb], o[qb][db]);
-    __builtin_amdgcn_sched_barrier(0);
-  } else if (!SWZ) {
-    const uint16_t* v0 = Vs + (kbase + 4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3);
-    const uint16_t* v1 = v0 + 16 * VP;
-#pragma unroll
-    for (int db = 0; db < DV; ++db) {
-      const u32x2 lo = lds_read_tr4(v0 + 16 * db);
-      const u32x2 hi = lds_read_tr4(v1 + 16 * db);
-      const u32x4 vf1 = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf1, pk[qb], o[qb][db]);
-    }
-  } else {
-#pragma unroll
-    for (int db = 0; db < DV; ++db) {
-      const u32x4 v1 = read_vfrag1<VP, SWZ>(Vs, kbase, db, c16, g4);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(v1, pk[qb], o[qb][db]);
-    }
+    for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf1, pk[qb], o[qb][db]);
   }
 }
 
-// Both 32-key steps of a 64-key tile; the second step's K fragments are read
-// during the first step's products.
-template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SWZ, bool SOFTCAP, bool EARLY>
+// Both 32-key steps of a 64-key tile.
+template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SOFTCAP>
 __device__ __forceinline__ void tile_pair(const uint16_t* Ks, const uint16_t* Vs, int k0, bool full,
                                           const u32x4 (&qf)[NQB][DQK], const int (&qpos)[NQB],
                                           float (&m_e)[NQB], float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
                                           const KernelArgs& a, int c16, int g4) {
-  u32x4 kf[2][DQK];
-  if (EARLY) {
-    read_kfrag<DQK, KP, SWZ>(kf, Ks, 0, c16, g4);
-    if (full) {
-      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, false, true, true>(Ks, Vs, 0, k0, kf, qf, qpos,
-                                                                          m_e, l_p, o, a, c16, g4);
-      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, false, false, true>(Ks, Vs, 32, k0, kf, qf, qpos,
-                                                                           m_e, l_p, o, a, c16, g4);
-    } else {
-      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, true, true, true>(Ks, Vs, 0, k0, kf, qf, qpos,
-                                                                         m_e, l_p, o, a, c16, g4);
-      tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, true, false, true>(Ks, Vs, 32, k0, kf, qf, qpos,
-                                                                          m_e, l_p, o, a, c16, g4);
-    }
-  } else {
 #pragma unroll
-    for (int kb = 0; kb < 64; kb += 32) {
-      if (full)
-        tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, false, false, false>(Ks, Vs, kb, k0, kf, qf, qpos,
-                                                                              m_e, l_p, o, a, c16, g4);
-      else
-        tile_step<T, DQK, DV, NQB, KP, VP, SWZ, SOFTCAP, true, false, false>(Ks, Vs, kb, k0, kf, qf, qpos,
-                                                                             m_e, l_p, o, a, c16, g4);
-    }
+  for (int kb = 0; kb < 64; kb += 32) {
+    if (full)
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
+    else
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
   }
 }
 
@@ -653,8 +535,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
     }
     // Two 32-key steps per tile; K fragments of the second step are read
     // during the first step's products.
-    tile_pair<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, false>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16,
-                                                        g4);
+    tile_pair<T, DQK, DV, NQB, KP, VP, SOFTCAP>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16, g4);
     if (t + 1 < t_end) {
       uint16_t* nxt = smem + (cur ^ 1) * STAGE;
       kt.store(nxt, tid);
@@ -688,15 +569,19 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 // of fp32 and bf16: no running maximum and no rescale are needed.  Otherwise
 // the running maximum is kept with the lazy rescale.
 //
-// LDS: four stages of one 64-key tile, all K tiles first, then all V tiles,
-// filled by direct global-to-LDS loads.  Tile t+3 is requested once every
-// wave is past the first half of tile t, so each tile has two tiles of time
-// to land.  The tile loop is unrolled over the four stages, so every fragment
-// read is one of twelve per-lane base addresses plus a constant offset.
+// Workgroup: four waves (one per SIMD), 128 rows, one 32-key tile per step.
+// LDS holds five stages of one K and one V tile (16 KB per stage pair), all
+// K tiles first, then all V tiles, filled by direct global-to-LDS loads: two
+// workgroups fit in one CU, so every SIMD runs waves of two independent
+// workgroups whose barriers and load waits do not line up.  Tile j+3 is
+// requested once every wave is past step j-1 (the last reader of tile j-2's
+// stage), two steps before it is first read.  The step loop is unrolled over
+// the five stages, so every fragment read is one of twelve per-lane base
+// addresses plus a constant offset.
 // ---------------------------------------------------------------------------
-constexpr int kPipeStages = 4;
-constexpr int kPipeTile = 64 * 128;                    // elements of one K or V tile
-constexpr int kPipeVRegion = kPipeStages * kPipeTile;  // first V tile (elements)
+constexpr int kPipe4Stages = 5;
+constexpr int kPipe4Tile = 32 * 128;                       // elements of one K or V tile
+constexpr int kPipe4VRegion = kPipe4Stages * kPipe4Tile;  // first V tile (elements)
 
 template <typename T>
 struct OnesOperand;
@@ -868,242 +753,9 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
   }
 }
 
-template <typename T, bool SOFTCAP, bool FIXREF>
-__global__ __launch_bounds__(512) void prefill_pipe_kernel(KernelArgs a) {
-  constexpr int NWAVES = 8, D = 128, KEYS = 64, TILE = kPipeTile;
-  constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row direct-to-LDS loads per wave per tensor
-  static_assert(IPW == 2, "the wait counts below assume two loads per tensor per wave");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kPipeStages * TILE];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int g4 = lane >> 4, c16 = lane & 15;
-
-  const int bid = blockIdx.x;
-  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
-  // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
-  // range of (unit, position block) pairs: the blocks of one unit then share
-  // their K/V tiles in one L2.
-  int lin = bid;
-  if ((gridDim.x & 7) == 0) lin = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
-  const int pblk = lin % a.n_pos_blk;
-  const int unit = lin / a.n_pos_blk;  // b * Hkv + kvh
-  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
-  const int G = a.G;
-  const int q0 = pblk * a.m;
-  const int m_eff = min(a.m, a.Lq - q0);
-  const int off = a.Lkv - a.Lq;
-
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
-  uint16_t* og = static_cast<uint16_t*>(a.out);
-
-  // Key band of this block of positions, in tiles.
-  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
-  int key_lo = 0, key_hi = a.Lkv - 1;
-  if (a.causal) key_hi = min(key_hi, pos_max);
-  if (a.window > 0) {
-    key_lo = max(0, pos_min - a.window + 1);
-    if (!a.causal) key_hi = min(key_hi, pos_max + a.window - 1);
-  }
-  const int t_begin = key_lo / KEYS, t_end = key_hi / KEYS + 1;
-
-  // Q first: the direct-to-LDS loads are counted after it, so waiting for
-  // the first tile also waits for Q.
-  u32x4 qf[2][4];
-  int rconst[2], span[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = (wave * 2 + qb) * 16 + c16;
-    const int pl = r / G, hr = r % G;
-    const bool ok = pl < m_eff;
-    const int pos = q0 + pl + off;
-    const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (ok ? q0 + pl : 0)) * D;
-    load_q<4>(qf[qb], qg + ro, ok, D, g4);
-    // Visible keys of this row: [lo, hi].
-    const int lo = a.window > 0 ? pos - a.window + 1 : 0;
-    int hi = a.Lkv - 1;
-    if (a.causal) hi = min(hi, pos);
-    else if (a.window > 0) hi = min(hi, pos + a.window - 1);
-    rconst[qb] = 4 * g4 - lo;
-    span[qb] = hi - lo;
-  }
-
-  int voffK[IPW], voffV[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int row = 4 * (wave * IPW + j) + (lane >> 4), slot = lane & 15;
-    voffK[j] = (row * D + ((slot ^ (row & 15)) << 3)) * 2;
-    voffV[j] = (row * D + ((slot ^ (2 * (row & 7))) << 3)) * 2;
-  }
-  auto fetch = [&](int t, uint16_t* kst, uint16_t* vst) {
-    // (Forced into scalar registers: the descriptor must be uniform.)
-    const int k0 = wave_uniform(t * KEYS);
-    const uint32_t bytes = (uint32_t)wave_uniform((a.Lkv - k0) * (D * 2));
-    const u32x4 rk = raw_rsrc(kg + (size_t)k0 * D, bytes);
-    const u32x4 rv = raw_rsrc(vg + (size_t)k0 * D, bytes);
-#pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int row0 = (wave * IPW + j) * 4 * D;
-      lds_dma16_async(rk, kst + row0, voffK[j]);
-      lds_dma16_async(rv, vst + row0, voffV[j]);
-    }
-  };
-
-  uint16_t* const sk = smem;
-  uint16_t* const sv = smem + kPipeVRegion;
-  fetch(t_begin, sk, sv);
-  if (t_begin + 1 < t_end) fetch(t_begin + 1, sk + TILE, sv + TILE);
-  if (t_begin + 2 < t_end) fetch(t_begin + 2, sk + 2 * TILE, sv + 2 * TILE);
-  // Stage 3's V tile stands in for "the tile before the first" (with zero
-  // probabilities): clear it so that it holds finite values.
-  {
-    uint16_t* z = sv + 3 * TILE;
-#pragma unroll
-    for (int i = 0; i < TILE / (8 * 512); ++i)
-      *reinterpret_cast<u32x4*>(z + (i * 512 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  PipeAddr ad;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) ad.ka[t] = c16 * 128 + (((4 * t + g4) ^ c16) << 3);
-  {
-    const int row = 4 * g4 + (c16 >> 2);
-    const int sw = 2 * (row & 7);
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      ad.va[db] = row * 128 + (((2 * db + ((c16 & 3) >> 1)) ^ sw) << 3) + 4 * (c16 & 1);
-  }
-
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (t_begin + 2 < t_end)
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tiles t_begin+1, +2 may still fly
-  else if (t_begin + 1 < t_end)
-    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-
-  float m_e[2] = {kNegInf, kNegInf};
-  f32x4 o[2][8], ls[2];
-  f32x4 sa[2][2], sb[2][2];
-  u32x4 pa[2], pb[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    pb[qb] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // Scores of the first step (stage 0, tile rows 0..31).
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc = Elem<T>::mfma(*reinterpret_cast<const u32x4*>(sk + ad.ka[t] + hh * 16 * 128), qf[qb][t], acc);
-      sa[qb][hh] = acc;
-    }
-
-  auto step_full = [&](int kg0) {
-    bool full = kg0 + 32 <= a.Lkv;
-    if (a.causal) full = full && (kg0 + 31 <= pos_min);
-    if (a.window > 0) {
-      full = full && (pos_max - kg0 < a.window);
-      if (!a.causal) full = full && (kg0 + 31 - pos_min < a.window);
-    }
-    return full;
-  };
-  // Tile t in stage ST (compile time).  First half: softmax of keys
-  // [64t, 64t+32), scores of [64t+32, 64t+64), P.V of the previous tile's
-  // second half (stage ST-1).  Second half: softmax of [64t+32, 64t+64),
-  // scores of the next tile's first half (stage ST+1; discarded after the
-  // last tile), P.V of this tile's first half.
-  auto tile = [&](auto stc, int t) {
-    constexpr int ST = decltype(stc)::value;
-    constexpr int SP = (ST + kPipeStages - 1) % kPipeStages, SN = (ST + 1) % kPipeStages;
-    {
-      const int kg0 = t * KEYS;
-      const int ub[2] = {kg0 + rconst[0], kg0 + rconst[1]};
-      pipe_step<T, SOFTCAP, FIXREF, ST * TILE + 32 * 128, SP * TILE + 32 * 128>(!step_full(kg0), sk, sv, ad, sa, sb, pb,
-                                                                                pa, qf, o, ls, m_e, ub, span, a);
-    }
-    // Tile t+1 must be in LDS, and every wave past the first half (so done
-    // with tile t-1, whose stage now takes tile t+3).
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (t + 2 < t_end)
-      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): tile t+2 may still fly
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (t + 3 < t_end) fetch(t + 3, sk + SP * TILE, sv + SP * TILE);
-    {
-      const int kg0 = t * KEYS + 32;
-      const int ub[2] = {kg0 + rconst[0], kg0 + rconst[1]};
-      pipe_step<T, SOFTCAP, FIXREF, SN * TILE, ST * TILE>(!step_full(kg0), sk, sv, ad, sb, sa, pa, pb, qf, o, ls, m_e,
-                                                          ub, span, a);
-    }
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  int t = t_begin, last = 0;
-  while (true) {
-    tile(S0{}, t);
-    if (++t >= t_end) { last = 0; break; }
-    tile(S1{}, t);
-    if (++t >= t_end) { last = 1; break; }
-    tile(S2{}, t);
-    if (++t >= t_end) { last = 2; break; }
-    tile(S3{}, t);
-    if (++t >= t_end) { last = 3; break; }
-  }
-  // P.V and row sums of the last step (second half of the last tile).
-  {
-    const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
-                        OnesOperand<T>::kPair};
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const uint16_t* v0 = sv + ad.va[db] + last * TILE + 32 * 128;
-      const u32x2 lo = lds_read_tr4(v0);
-      const u32x2 hi = lds_read_tr4(v0 + 16 * 128);
-      const u32x4 v1 = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[qb][db] = Elem<T>::mfma(v1, pb[qb], o[qb][db]);
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) ls[qb] = Elem<T>::mfma(ones, pb[qb], ls[qb]);
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = (wave * 2 + qb) * 16 + c16;
-    const int pl = r / G, hr = r % G;
-    if (pl < m_eff) {
-      const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + q0 + pl) * D;
-      store_row<T, 8>(og + ro, o[qb], 1.0f / ls[qb][0], D, g4);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// The same pipelined steps with four waves (one per SIMD) and 128 rows per
-// workgroup, one 32-key tile per step, five LDS stages of 16 KB: two
-// workgroups fit in one CU's LDS, so every SIMD runs waves of two
-// independent workgroups, whose barriers and load waits do not line up.
-// Tile j+3 is requested once every wave is past step j-1 (the last reader
-// of tile j-2's stage), two steps before it is first read.
+// The pipelined prefill kernel for head size 128 (layout and schedule above).
 // ---------------------------------------------------------------------------
-constexpr int kPipe4Stages = 5;
-constexpr int kPipe4Tile = 32 * 128;                       // elements of one K or V tile
-constexpr int kPipe4VRegion = kPipe4Stages * kPipe4Tile;  // first V tile (elements)
-
 template <typename T, bool SOFTCAP, bool FIXREF>
 __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   constexpr int NWAVES = 4, D = 128, KEYS = 32, TILE = kPipe4Tile, NS = kPipe4Stages;
@@ -1450,7 +1102,6 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 kf_unused[2][DQK];
   for (int it = 0; it < ntile; ++it) {
     const int t = tile_at(it);
     const int k0 = t * KEYS;
@@ -1476,11 +1127,9 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
     }
     if (full)
-      tile_step<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, false, false, false>(
-          Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
     else
-      tile_step<T, DQK, DV, NQB, KP, VP, false, SOFTCAP, true, false, false>(
-          Ks, Vs, 32 * wave, k0, kf_unused, qf, qpos, m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
   }
 
   // ---- merge the wave states (fixed order) ------------------------------------
