@@ -460,7 +460,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   const int g4 = lane >> 4, c16 = lane & 15;
 
   const int bid = blockIdx.x;
-  const int pblk = bid % a.n_pos_blk;
+  const int pblk = a.n_pos_blk - 1 - bid % a.n_pos_blk;  // longest key bands first (causal)
   const int unit = bid / a.n_pos_blk;  // b * Hkv + kvh
   const int kvh = unit % a.Hkv, b = unit / a.Hkv;
   const int G = a.G, d = a.d;
@@ -771,10 +771,13 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
   // range of (unit, position block) pairs: the blocks of one unit then share
   // their K/V tiles in one L2.
+  // Within a unit the blocks are taken last first: under a causal mask the
+  // later blocks have the longer key bands, and starting the longest work
+  // first leaves shorter blocks to even out the end of the launch.
   const int bid = blockIdx.x;
   int lin = bid;
   if ((gridDim.x & 7) == 0) lin = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
-  const int pblk = lin % a.n_pos_blk;
+  const int pblk = a.n_pos_blk - 1 - lin % a.n_pos_blk;
   const int unit = lin / a.n_pos_blk;  // b * Hkv + kvh
   const int kvh = unit % a.Hkv, b = unit / a.Hkv;
   const int G = a.G;
