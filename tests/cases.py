@@ -122,6 +122,16 @@ CASES = [
     # prefill kernel (256-row workgroups), full parity
     Case("prefill_big_g16_d128", 1, 256, 16, 256, 256, 128, causal=True, window=90, seed=57),
     Case("prefill_big_g16_d96_noncausal", 1, 256, 16, 256, 200, 96, seed=58),
+    # head sizes between the common ones: padded Q.K^T (to 64/96/128) and
+    # P.V (to 64/80/128) widths on both kernels
+    Case("prefill_big_g16_d112_window_cap", 1, 256, 16, 256, 256, 112, causal=True, window=60, softcap=25.0,
+         seed=59),
+    Case("prefill_big_g8_d120_noncausal", 1, 256, 32, 256, 256, 120, seed=60),
+    Case("split_d120_g4", 1, 16, 4, 40, 900, 120, causal=True, seed=61),
+    Case("decode_d80_g8_cap", 2, 16, 2, 1, 1500, 80, causal=True, softcap=40.0, seed=62),
+    Case("split_d40_g5_window", 1, 10, 2, 120, 150, 40, causal=True, window=50, seed=63),
+    Case("decode_d104_g12", 1, 24, 2, 1, 700, 104, causal=True, seed=64),
+    Case("split_d56_g7_fp16", 1, 14, 2, 50, 400, 56, dtype="fp16", seed=65),
 ]
 
 CASES_BY_NAME = {c.name: c for c in CASES}
