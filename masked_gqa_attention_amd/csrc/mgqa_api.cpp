@@ -182,6 +182,11 @@ static KernelArgs make_args(const Plan& p, const void* q, const void* k, const v
   a.m = p.m;
   a.n_pos_blk = p.n_pos_blk;
   a.nsplit = p.nsplit;
+  a.div_g = make_fastdiv((uint32_t)a.G);
+  a.div_hkv = make_fastdiv((uint32_t)Hkv);
+  a.div_npos = make_fastdiv((uint32_t)p.n_pos_blk);
+  a.div_nsplit = make_fastdiv((uint32_t)p.nsplit);
+  a.nwg = (int)p.workgroups;
   a.tiles_per_split = p.tiles_per_split;
   a.nrows = p.m * a.G;
   if (ws) {

@@ -24,6 +24,22 @@ constexpr int kSplitWideMaxDv = 6;  // P.V 16-column blocks up to which 3 and 4 
 
 enum Path { kPathPrefill = 0, kPathSplit = 1 };
 
+// Division by a launch constant without a divide sequence: for 0 <= x < 2^31,
+// x / d == (x * m) >> (31 + s) with s = ceil(log2 d) and m = ceil(2^(31+s) / d)
+// (m < 2^32; the rounding error x*(m - 2^(31+s)/d) / 2^(31+s) stays below 2^-s
+// <= 1/d, so it never carries past an integer).
+struct FastDiv {
+  uint32_t m;
+  uint32_t s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1u << s) < d) ++s;
+  const uint64_t num = 1ull << (31 + s);
+  return FastDiv{(uint32_t)((num + d - 1) / d), s};
+}
+
 // Everything a kernel needs, passed by value.
 struct KernelArgs {
   const void* q;
@@ -48,6 +64,8 @@ struct KernelArgs {
   int nsplit;         // key splits per position block
   int tiles_per_split;
   int nrows;          // m*G rows of a full position block
+  FastDiv div_g, div_hkv, div_npos, div_nsplit;  // for G, Hkv, n_pos_blk, nsplit
+  int nwg;            // workgroups of the launch (the grid size, read with the other arguments)
 };
 
 struct Plan {

@@ -295,6 +295,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// x / d for 0 <= x < 2^31 with the launch's precomputed (m, s) for d: one
+// multiply-high and a shift instead of a divide sequence (see FastDiv).
+__device__ __forceinline__ int fdiv(int x, FastDiv f) {
+  return (int)(((uint64_t)(uint32_t)x * f.m) >> (31 + f.s));
+}
 // Raw buffer descriptor words (base, stride 0, num_records = bytes, the same
 // format word as make_rsrc) for the inline-assembly load below.
 __device__ __forceinline__ u32x4 raw_rsrc(const void* p, uint32_t bytes) {
@@ -459,10 +464,16 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
 
+  // Every argument the first loads depend on, asked for at once, so that
+  // their loads leave in one batch and cost one round trip.
+  asm volatile("" : : "s"(a.kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
+               "s"(a.G), "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.causal), "s"(a.window), "s"(a.div_g.m),
+               "s"(a.div_g.s), "s"(a.div_npos.m), "s"(a.div_npos.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s),
+               "s"(a.nwg));
   const int bid = blockIdx.x;
-  const int pblk = a.n_pos_blk - 1 - bid % a.n_pos_blk;  // longest key bands first (causal)
-  const int unit = bid / a.n_pos_blk;  // b * Hkv + kvh
-  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int unit = fdiv(bid, a.div_npos);  // b * Hkv + kvh
+  const int pblk = a.n_pos_blk - 1 - (bid - unit * a.n_pos_blk);  // longest key bands first (causal)
+  const int b = fdiv(unit, a.div_hkv), kvh = unit - b * a.Hkv;
   const int G = a.G, d = a.d;
   const int q0 = pblk * a.m;
   const int m_eff = min(a.m, a.Lq - q0);
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int r = (wave * NQB + qb) * 16 + c16;
-    const int pl = r / G, hr = r % G;
+    const int pl = fdiv(r, a.div_g), hr = r - pl * G;
     rok[qb] = pl < m_eff;
     const int pos = q0 + pl;
     qpos[qb] = pos + off;
@@ -774,12 +785,18 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   // Within a unit the blocks are taken last first: under a causal mask the
   // later blocks have the longer key bands, and starting the longest work
   // first leaves shorter blocks to even out the end of the launch.
+  // Every argument the first loads depend on, asked for at once, so that
+  // their loads leave in one batch and cost one round trip.
+  asm volatile("" : : "s"(a.kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
+               "s"(a.G), "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.causal), "s"(a.window), "s"(a.div_g.m),
+               "s"(a.div_g.s), "s"(a.div_npos.m), "s"(a.div_npos.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s),
+               "s"(a.nwg));
   const int bid = blockIdx.x;
   int lin = bid;
-  if ((gridDim.x & 7) == 0) lin = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
-  const int pblk = a.n_pos_blk - 1 - lin % a.n_pos_blk;
-  const int unit = lin / a.n_pos_blk;  // b * Hkv + kvh
-  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  if ((a.nwg & 7) == 0) lin = (bid & 7) * (a.nwg >> 3) + (bid >> 3);
+  const int unit = fdiv(lin, a.div_npos);  // b * Hkv + kvh
+  const int pblk = a.n_pos_blk - 1 - (lin - unit * a.n_pos_blk);
+  const int b = fdiv(unit, a.div_hkv), kvh = unit - b * a.Hkv;
   const int G = a.G;
   const int q0 = pblk * a.m;
   const int m_eff = min(a.m, a.Lq - q0);
@@ -807,7 +824,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = (wave * 2 + qb) * 16 + c16;
-    const int pl = r / G, hr = r % G;
+    const int pl = fdiv(r, a.div_g), hr = r - pl * G;
     const bool ok = pl < m_eff;
     const int pos = q0 + pl + off;
     const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (ok ? q0 + pl : 0)) * D;
@@ -985,7 +1002,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = (wave * 2 + qb) * 16 + c16;
-    const int pl = r / G, hr = r % G;
+    const int pl = fdiv(r, a.div_g), hr = r - pl * G;
     if (pl < m_eff) {
       const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + q0 + pl) * D;
       store_row<T, 8>(og + ro, o[qb], 1.0f / ls[qb][0], D, g4);
@@ -1029,13 +1046,20 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
   // range of (group, split) pairs: the position blocks of one unit, which
   // read the same K/V rows, then share them in one L2.
+  // Every argument the first tile request depends on, asked for at once, so
+  // that their loads leave in one batch and cost one round trip.
+  const long long kv_stride = a.kv_stride;
+  asm volatile("" : : "s"(kv_stride), "s"(a.k), "s"(a.v), "s"(a.nsplit), "s"(a.n_pos_blk), "s"(a.Hkv),
+               "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.d), "s"(a.causal), "s"(a.window),
+               "s"(a.tiles_per_split), "s"(a.div_nsplit.m), "s"(a.div_nsplit.s), "s"(a.div_npos.m),
+               "s"(a.div_npos.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s), "s"(a.nwg));
   int lin = blockIdx.x;
-  if ((gridDim.x & 7) == 0) lin = (lin & 7) * (int)(gridDim.x >> 3) + (lin >> 3);
-  const int split = lin % a.nsplit;
-  const int grp = lin / a.nsplit;  // unit * n_pos_blk + position block
-  const int pblk = grp % a.n_pos_blk;
-  const int unit = grp / a.n_pos_blk;
-  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  if ((a.nwg & 7) == 0) lin = (lin & 7) * (a.nwg >> 3) + (lin >> 3);
+  const int grp = fdiv(lin, a.div_nsplit);  // unit * n_pos_blk + position block
+  const int split = lin - grp * a.nsplit;
+  const int unit = fdiv(grp, a.div_npos);
+  const int pblk = grp - unit * a.n_pos_blk;
+  const int b = fdiv(unit, a.div_hkv), kvh = unit - b * a.Hkv;
   const int G = a.G, d = a.d;
   const int off = a.Lkv - a.Lq;
   const int q0 = pblk * a.m;
@@ -1043,8 +1067,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   const int nrows = m_eff * G;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * a.kv_stride;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * a.kv_stride;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * kv_stride;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * kv_stride;
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
   // Key band of this block of positions, in tiles, and this split's share.
@@ -1074,8 +1098,10 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   // addresses with the same alignment (which concentrates the first requests
   // on a few memory channels).  The softmax merge is order independent; the
   // order is a fixed function of the shape, so results stay reproducible.
+  // The start is 5*lin modulo the largest power of two <= ntile (a mask, no
+  // division, and always < ntile).
   const int ntile = max(t1 - t0, 0);
-  const int rot = ntile > 0 ? (int)(((unsigned)lin * 5u) % (unsigned)ntile) : 0;
+  const int rot = ntile > 0 ? (int)(((unsigned)lin * 5u) & ((1u << (31 - __builtin_clz((unsigned)ntile))) - 1u)) : 0;
   auto tile_at = [&](int i) { const int r = i + rot; return t0 + (r >= ntile ? r - ntile : r); };
   if (ntile > 0) {
     fetch_k(tile_at(0) * KEYS);
@@ -1089,7 +1115,7 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   for (int qb = 0; qb < NQB; ++qb) {
     const int r = 16 * qb + c16;
     const bool rok = r < nrows;
-    const int pl = r / G, hr = r % G;
+    const int pl = fdiv(r, a.div_g), hr = r - pl * G;
     const size_t roff = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (rok ? q0 + pl : 0)) * d;
     qpos[qb] = q0 + pl + off;
     load_q<DQK>(qf[qb], qg + roff, rok, d, g4);
@@ -1144,8 +1170,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int JN = (NQB * 16 * CPR + NT - 1) / NT;
   const int rstride = a.nrows;  // rows of a full block: partial layout stride
   const int pidx = (grp * a.nsplit + split) * rstride;
-  const uint32_t o_bytes = (uint32_t)gridDim.x * rstride * DVP * 4;
-  const uint32_t ml_bytes = (uint32_t)gridDim.x * rstride * 8;
+  const uint32_t o_bytes = (uint32_t)a.nwg * rstride * DVP * 4;
+  const uint32_t ml_bytes = (uint32_t)a.nwg * rstride * 8;
   const auto rs_o = make_rsrc(a.ws_o, o_bytes);
   const auto rs_ml = make_rsrc(a.ws_ml, ml_bytes);
   __syncthreads();  // the tiles are no longer read
@@ -1182,7 +1208,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     if (a.nsplit == 1) {
       if (4 * c4 < d) {
         const float inv = 1.0f / L;
-        const size_t oo = (((size_t)b * a.Hq + kvh * G + r % G) * a.Lq + q0 + r / G) * d + 4 * c4;
+        const int pr = fdiv(r, a.div_g);
+        const size_t oo = (((size_t)b * a.Hq + kvh * G + (r - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
         *reinterpret_cast<u32x2*>(og + oo) =
             u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
       }
@@ -1248,7 +1275,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     }
     if (4 * c4 < d) {
       const float inv = 1.0f / Lg;
-      const size_t oo = (((size_t)b * a.Hq + kvh * G + row % G) * a.Lq + q0 + row / G) * d + 4 * c4;
+      const int pr = fdiv(row, a.div_g);
+      const size_t oo = (((size_t)b * a.Hq + kvh * G + (row - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
       *reinterpret_cast<u32x2*>(og + oo) =
           u32x2{Elem<T>::pack2(og4[0] * inv, og4[1] * inv), Elem<T>::pack2(og4[2] * inv, og4[3] * inv)};
     }
