@@ -175,3 +175,14 @@ def test_workspace_layout_fits():
             assert info["workspace_bytes"] >= need
         else:
             assert info["workspace_bytes"] == 0
+
+
+def test_encoder_shapes_split_keys_when_row_blocks_are_few():
+    """Short non-causal sequences with few heads: the row blocks alone would
+    leave most compute units idle, so the plan splits the key axis too; with
+    16 heads the row blocks already fill the chip and there is no split."""
+    for H, want_split in ((1, True), (2, True), (4, True), (16, False)):
+        rc, info = _lib.attn_plan(1, H, H, 729, 729, 72, 0, 0, 0.0)
+        assert rc == 0 and info["path"] == 1, info
+        assert (info["nsplit"] > 1) == want_split, (H, info)
+        assert info["workgroups"] >= 256 or info["nsplit"] > 1, (H, info)
