@@ -133,14 +133,18 @@ int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const floa
  *         workgroups, split the key band of its rows)
  * info[1] workgroups launched
  * info[2] query rows (head, position pairs) per workgroup
- * info[3] key splits across workgroups per block of rows (1 on the prefill path)
+ * info[3] key splits per block of rows (1 on the prefill path); workgroups =
+ *         blocks of rows x info[3] x info[8]
  * info[4] keys per tile
  * info[5] padded head size used for Q.K^T (multiple of 32)
  * info[6] padded head size used for P.V (multiple of 16)
  * info[7] workspace bytes
+ * info[8] column slices: workgroups sharing one key range of a block of rows,
+ *         each computing P.V for its share of the head size (1, or 2 when a
+ *         single 16-row block has many key splits; split path only)
  * Returns 0 or a validation error code (then info is untouched). */
 int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d,
-              int causal, int window, float softcap, int dtype, long long info[8]);
+              int causal, int window, float softcap, int dtype, long long info[9]);
 
 /* Static text for an error code (never NULL). */
 const char* attn_error_string(int code);

@@ -106,12 +106,12 @@ def attn_workspace_bytes(B, Hq, Hkv, Lq, Lkv, d, causal, window) -> int:
 
 
 PLAN_FIELDS = ("path", "workgroups", "rows_per_wg", "nsplit", "keys_per_tile", "d_qk_pad",
-               "d_pv_pad", "workspace_bytes")
+               "d_pv_pad", "workspace_bytes", "ncol")
 
 
 def attn_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype=MGQA_BF16):
     """Returns (code, dict) -- dict is empty when code != 0."""
-    info = (ctypes.c_longlong * 8)()
+    info = (ctypes.c_longlong * len(PLAN_FIELDS))()
     rc = load().attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window), float(softcap),
                           int(dtype), info)
     if rc != 0:

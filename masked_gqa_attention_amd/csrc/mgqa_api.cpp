@@ -19,6 +19,8 @@ constexpr int kCUs = 256;              // MI355X compute units
 constexpr long long kSplitTarget = 256;
 constexpr int kMaxCounters = 256;  // leading counter block
 static_assert(kSplitTarget <= kMaxCounters, "split plans need one counter per group");
+// Splits of one key band from which two column halves pay off.
+constexpr long long kHalfColumnsMinSplits = 8;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -113,6 +115,7 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   const long long groups = units * p.n_pos_blk;
   long long ns = 1;
   int tps = 1 << 30;  // one split: the whole band
+  int ncol = 1;
   if (groups < kSplitTarget) {
     // Largest band (in tiles) of any position block (fewer than kSplitTarget blocks here).
     int max_tiles = 1;
@@ -126,16 +129,28 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
     }
     ns = (kSplitTarget + groups - 1) / groups;
     if (ns > max_tiles) ns = max_tiles;
+    // Column halves: with many splits of one 16-row block the last arrival
+    // reads nsplit partials of the whole head size.  Two workgroups per key
+    // range, each with half of V's columns, halve both the number of splits
+    // and the width of each partial (a quarter of the merge reads), for the
+    // same workgroup count; the pair reads the same K rows at the same time
+    // on one XCD, so K comes from HBM once.
+    if (ns >= kHalfColumnsMinSplits && p.dv == 8 && p.nqb == 1 && groups * 2 <= kMaxCounters) {
+      ncol = 2;
+      ns = (kSplitTarget + 2 * groups - 1) / (2 * groups);
+      if (ns > max_tiles) ns = max_tiles;
+    }
     tps = (int)((max_tiles + ns - 1) / ns);
     ns = (max_tiles + tps - 1) / tps;
   }
   p.nsplit = (int)ns;
   p.tiles_per_split = tps;
-  p.workgroups = groups * ns;
+  p.ncol = ns > 1 ? ncol : 1;
+  p.workgroups = groups * ns * p.ncol;
   if (ns > 1) {
     const size_t nrows = (size_t)p.m * G;
     const size_t o_bytes = (size_t)groups * ns * nrows * (p.dv * 16) * sizeof(float);
-    const size_t ml_bytes = (size_t)groups * ns * nrows * 2 * sizeof(float);
+    const size_t ml_bytes = (size_t)groups * p.ncol * ns * nrows * 2 * sizeof(float);
     // Key splits happen only with fewer than kSplitTarget groups, so the
     // counters of every plan fit the same leading kMaxCounters words: no plan
     // writes partials there, and the counters a call leaves at zero stay zero
@@ -146,7 +161,7 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
     p.ws_bytes = align_up(p.ws_o_off + o_bytes, 256);
   }
   if (p.workgroups >= (1LL << 31)) return MGQA_ERR_RANGE;
-  if (ns > 1 && groups > kMaxCounters) return MGQA_ERR_RANGE;  // cannot happen: see the counter layout
+  if (ns > 1 && groups * p.ncol > kMaxCounters) return MGQA_ERR_RANGE;  // cannot happen: see the counter layout
   // 32-bit byte offsets of the partials inside the kernel.
   if (p.ws_bytes >= (1ULL << 31)) return MGQA_ERR_RANGE;
   *plan = p;
@@ -206,7 +221,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 extern "C" {
 
-int attn_version(void) { return 100; }
+int attn_version(void) { return 101; }
 
 const char* attn_error_string(int code) {
   switch (code) {
@@ -228,7 +243,7 @@ const char* attn_error_string(int code) {
 }
 
 int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
-              float softcap, int dtype, long long info[8]) {
+              float softcap, int dtype, long long info[9]) {
   if (!info) return MGQA_ERR_NULL;
   Plan p;
   const int err = make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, &p);
@@ -241,6 +256,7 @@ int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   info[5] = p.dqk * 32;
   info[6] = p.dv * 16;
   info[7] = (long long)p.ws_bytes;
+  info[8] = p.ncol > 0 ? p.ncol : 1;
   return MGQA_OK;
 }
 

@@ -80,6 +80,7 @@ struct Plan {
   int n_pos_blk;      // position blocks per (batch, kv head)
   int nsplit;
   int tiles_per_split;
+  int ncol;           // split path: workgroups sharing one key range, each with 1/ncol of V's columns
   long long workgroups;
   size_t ws_bytes;
   size_t ws_o_off, ws_ml_off, ws_cnt_off;

@@ -245,14 +245,15 @@ struct RowTile {
   int voff[NOFF];
   int vstep;  // bytes between consecutive loads of a thread (COMPACT only)
 
-  __device__ __forceinline__ void init(int d, int tid) {
+  // col0: first column of the rows this tile holds (a multiple of 8).
+  __device__ __forceinline__ void init(int d, int tid, int col0 = 0) {
     vstep = (NT / CH) * d * 2;
 #pragma unroll
     for (int it = 0; it < NOFF; ++it) {
       const int c = tid + it * NT;
       const int key = c / CH, ch = c % CH;
-      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (ch * 8 < d);
-      voff[it] = ok ? (key * d + ch * 8) * 2 : 0x7FFF0000;
+      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (col0 + ch * 8 < d);
+      voff[it] = ok ? (key * d + col0 + ch * 8) * 2 : 0x7FFF0000;
     }
   }
   // g: the (batch, kv head) unit's first row; loads keys k0 .. k0+KEYS-1.
@@ -268,7 +269,7 @@ struct RowTile {
   // (ring_start + j) % S; logical keys at or past Lkv, and chunks past d, read
   // as zero (offset beyond the unit's range).  g: the unit's slot 0.
   __device__ __forceinline__ void load_ring(const uint16_t* g, int k0, int Lkv, int d, int ring_start,
-                                            int S, int tid) {
+                                            int S, int tid, int col0 = 0) {
     const auto rs = make_rsrc(g, (uint32_t)S * (uint32_t)d * 2u);
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
@@ -276,8 +277,8 @@ struct RowTile {
       const int logical = k0 + c / CH, ch = c % CH;
       int slot = ring_start + logical;
       slot -= (slot >= S) ? S : 0;
-      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (logical < Lkv) && (ch * 8 < d);
-      const uint32_t vo = ok ? (uint32_t)(slot * d + ch * 8) * 2u : 0x7FFF0000u;
+      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (logical < Lkv) && (col0 + ch * 8 < d);
+      const uint32_t vo = ok ? (uint32_t)(slot * d + col0 + ch * 8) * 2u : 0x7FFF0000u;
       r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0));
     }
   }
@@ -1020,9 +1021,11 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 // the waves.  The wave states are merged in LDS in wave order, one 16-row block
 // at a time.  With one split the merged rows are the output; otherwise the
 // split's partial is written and the last split to arrive for the block merges
-// all partials in split order.
+// all partials in split order.  With many splits of one 16-row block the key
+// range of a split is shared by two workgroups, each with half of V's columns
+// (DV is then the half's width); each half merges its own partials.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING>
+template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING, int NCOL>
 __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KEYS = 32 * NW;
@@ -1053,10 +1056,15 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
                "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.d), "s"(a.causal), "s"(a.window),
                "s"(a.tiles_per_split), "s"(a.div_nsplit.m), "s"(a.div_nsplit.s), "s"(a.div_npos.m),
                "s"(a.div_npos.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s), "s"(a.nwg));
+  // With two column halves the pair sharing a key range is adjacent, so it
+  // runs on one XCD at the same time and K comes from HBM once.
   int lin = blockIdx.x;
   if ((a.nwg & 7) == 0) lin = (lin & 7) * (a.nwg >> 3) + (lin >> 3);
-  const int grp = fdiv(lin, a.div_nsplit);  // unit * n_pos_blk + position block
-  const int split = lin - grp * a.nsplit;
+  const int half = NCOL == 2 ? (lin & 1) : 0;
+  const int lsp = NCOL == 2 ? (lin >> 1) : lin;   // (group, split) index
+  const int col0 = half * DV * 16;                  // first V/O column of this workgroup
+  const int grp = fdiv(lsp, a.div_nsplit);  // unit * n_pos_blk + position block
+  const int split = lsp - grp * a.nsplit;
   const int unit = fdiv(grp, a.div_npos);
   const int pblk = grp - unit * a.n_pos_blk;
   const int b = fdiv(unit, a.div_hkv), kvh = unit - b * a.Hkv;
@@ -1084,13 +1092,13 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   RowTile<KEYS, DQK * 4, KP, NT> kt;
   RowTile<KEYS, DV * 2, VP, NT> vt;
   kt.init(d, tid);
-  vt.init(d, tid);
+  vt.init(d, tid, col0);
   auto fetch_k = [&](int k0) {
     if (RING) kt.load_ring(kg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
     else kt.load(kg, k0, a.Lkv, d);
   };
   auto fetch_v = [&](int k0) {
-    if (RING) vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
+    if (RING) vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid, col0);
     else vt.load(vg, k0, a.Lkv, d);
   };
   // The tiles of the range are visited in a rotated order that differs from
@@ -1169,7 +1177,11 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int CPR = DVP / 4;
   constexpr int JN = (NQB * 16 * CPR + NT - 1) / NT;
   const int rstride = a.nrows;  // rows of a full block: partial layout stride
+  // Partials: O rows [group][split][row] of NCOL*DVP floats (a column half
+  // writes its DVP of them); (max, sum) [group][half][split][row].
+  const int dvw = NCOL * DVP;
   const int pidx = (grp * a.nsplit + split) * rstride;
+  const int pml = ((grp * NCOL + half) * a.nsplit + split) * rstride;
   const uint32_t o_bytes = (uint32_t)a.nwg * rstride * DVP * 4;
   const uint32_t ml_bytes = (uint32_t)a.nwg * rstride * 8;
   const auto rs_o = make_rsrc(a.ws_o, o_bytes);
@@ -1206,17 +1218,18 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       }
     }
     if (a.nsplit == 1) {
-      if (4 * c4 < d) {
+      if (col0 + 4 * c4 < d) {
         const float inv = 1.0f / L;
         const int pr = fdiv(r, a.div_g);
-        const size_t oo = (((size_t)b * a.Hq + kvh * G + (r - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
+        const size_t oo =
+            (((size_t)b * a.Hq + kvh * G + (r - pr * G)) * a.Lq + q0 + pr) * d + col0 + 4 * c4;
         *reinterpret_cast<u32x2*>(og + oo) =
             u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
       }
     } else {
       // This split's partial, with device-coherent stores.
-      st_dev16(rs_o, ((pidx + r) * DVP + 4 * c4) * 4, acc);
-      if (c4 == 0) st_dev8(rs_ml, (pidx + r) * 8, f32x2{M, L});
+      st_dev16(rs_o, ((pidx + r) * dvw + col0 + 4 * c4) * 4, acc);
+      if (c4 == 0) st_dev8(rs_ml, (pml + r) * 8, f32x2{M, L});
     }
   }
   if (a.nsplit == 1) return;
@@ -1225,7 +1238,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   __syncthreads();
   if (tid == 0) {
     const unsigned prev =
-        __hip_atomic_fetch_add(a.ws_cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.ws_cnt + grp * NCOL + half, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == (unsigned)(a.nsplit - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -1237,7 +1251,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int CHUNK = 16;
   constexpr int JM = (16 * NQB * CPR + NT - 1) / NT;
   const int nch = nrows * CPR;
-  const int base = grp * a.nsplit * rstride;
+  const int base = grp * a.nsplit * rstride;                   // O rows of split 0
+  const int base_ml = (grp * NCOL + half) * a.nsplit * rstride;  // (max, sum) of split 0
 #pragma unroll
   for (int j = 0; j < JM; ++j) {
     const int q = tid + j * NT;
@@ -1251,9 +1266,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
 #pragma unroll
       for (int jj = 0; jj < CHUNK; ++jj) {
         const int sp = min(s0 + jj, a.nsplit - 1);
-        const int pr = base + sp * rstride + row;
-        ml[jj] = ld_dev8(rs_ml, pr * 8);
-        x[jj] = ld_dev16(rs_o, (pr * DVP + 4 * c4) * 4);
+        ml[jj] = ld_dev8(rs_ml, (base_ml + sp * rstride + row) * 8);
+        x[jj] = ld_dev16(rs_o, ((base + sp * rstride + row) * dvw + col0 + 4 * c4) * 4);
       }
       float mc = Mg;
 #pragma unroll
@@ -1273,15 +1287,17 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
         og4 += f * x[jj];
       }
     }
-    if (4 * c4 < d) {
+    if (col0 + 4 * c4 < d) {
       const float inv = 1.0f / Lg;
       const int pr = fdiv(row, a.div_g);
-      const size_t oo = (((size_t)b * a.Hq + kvh * G + (row - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
+      const size_t oo =
+          (((size_t)b * a.Hq + kvh * G + (row - pr * G)) * a.Lq + q0 + pr) * d + col0 + 4 * c4;
       *reinterpret_cast<u32x2*>(og + oo) =
           u32x2{Elem<T>::pack2(og4[0] * inv, og4[1] * inv), Elem<T>::pack2(og4[2] * inv, og4[3] * inv)};
     }
   }
-  if (tid == 0) __hip_atomic_store(a.ws_cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0)
+    __hip_atomic_store(a.ws_cnt + grp * NCOL + half, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_kernel(uint32_t* p, size_t n) {
@@ -1292,13 +1308,14 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the instantiated shapes.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NQB, bool SOFTCAP>
+template <typename T, int DQK, int DV, int NQB, bool SOFTCAP, int NCOL = 1>
 static void launch_split(const dim3& grid, const KernelArgs& args, hipStream_t st) {
   const dim3 block(64 * kSplitWaves);
   if (NQB == 1 && args.ring_start >= 0)
-    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, kSplitWaves, SOFTCAP, true>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, kSplitWaves, SOFTCAP, true, NCOL>), grid, block, 0, st,
+                       args);
   else
-    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, kSplitWaves, SOFTCAP, false>), grid, block, 0, st,
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, kSplitWaves, SOFTCAP, false, NCOL>), grid, block, 0, st,
                        args);
 }
 
@@ -1306,6 +1323,14 @@ template <typename T, int DQK, int DV, bool SOFTCAP>
 static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStream_t st) {
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathSplit) {
+    if (plan.ncol == 2) {
+      // Two column halves: each workgroup computes half of P.V's 16-column blocks.
+      if constexpr (DV == 8) {
+        launch_split<T, DQK, 4, 1, SOFTCAP, 2>(grid, args, st);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    }
     switch (plan.nqb) {
       case 1: launch_split<T, DQK, DV, 1, SOFTCAP>(grid, args, st); break;
       case 2: launch_split<T, DQK, DV, 2, SOFTCAP>(grid, args, st); break;

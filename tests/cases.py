@@ -132,6 +132,11 @@ CASES = [
     Case("split_d40_g5_window", 1, 10, 2, 120, 150, 40, causal=True, window=50, seed=63),
     Case("decode_d104_g12", 1, 24, 2, 1, 700, 104, causal=True, seed=64),
     Case("split_d56_g7_fp16", 1, 14, 2, 50, 400, 56, dtype="fp16", seed=65),
+    # one 16-row block per unit with many key splits: two workgroups per key
+    # range, each with half of V's columns
+    Case("halves_multitoken_g4_lq4_cap", 1, 8, 2, 4, 6000, 128, causal=True, softcap=20.0, seed=66),
+    Case("halves_decode_window_edges", 2, 16, 1, 1, 5000, 128, causal=True, window=1536, seed=67),
+    Case("halves_decode_fp16_cap", 1, 32, 2, 1, 4100, 128, causal=True, softcap=40.0, dtype="fp16", seed=68),
 ]
 
 CASES_BY_NAME = {c.name: c for c in CASES}

@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_version_and_error_strings():
-    assert _lib.attn_version() == 100
+    assert _lib.attn_version() == 101
     for code in range(-11, 1):
         s = _lib.error_string(code)
         assert s and s != "unknown error code"
@@ -153,7 +153,8 @@ def test_plans_for_workloads():
     # its splits times keys per split must not exceed the window plus a tile.
     info = paths["decode_gqa16_kv32768_w4096_cap30"]
     w = WORKLOADS["decode_gqa16_kv32768_w4096_cap30"]
-    assert info["workgroups"] == w.B * w.Hkv * info["nsplit"]
+    assert info["workgroups"] == w.B * w.Hkv * info["nsplit"] * info["ncol"]
+    assert info["ncol"] == 2  # one 16-row block per unit with many key splits: column halves
 
 
 def test_workspace_layout_fits():
@@ -168,10 +169,11 @@ def test_workspace_layout_fits():
         if info["nsplit"] > 1:
             G = Hq // Hkv
             rows = info["rows_per_wg"]
-            groups = info["workgroups"] // info["nsplit"]
-            assert groups < 256  # the counters fit the fixed block
+            groups = info["workgroups"] // (info["nsplit"] * info["ncol"])
+            assert groups * info["ncol"] <= 256  # the counters fit the fixed block
             m = min(rows // G, Lq)
-            need = 1024 + groups * info["nsplit"] * m * G * (info["d_pv_pad"] + 2) * 4
+            # O rows of the full padded width, (max, sum) per column slice
+            need = 1024 + groups * info["nsplit"] * m * G * (info["d_pv_pad"] + 2 * info["ncol"]) * 4
             assert info["workspace_bytes"] >= need
         else:
             assert info["workspace_bytes"] == 0
@@ -186,3 +188,20 @@ def test_encoder_shapes_split_keys_when_row_blocks_are_few():
         assert rc == 0 and info["path"] == 1, info
         assert (info["nsplit"] > 1) == want_split, (H, info)
         assert info["workgroups"] >= 256 or info["nsplit"] > 1, (H, info)
+
+
+def test_column_halves_plan():
+    """Many key splits of a single 16-row block: two workgroups per key range,
+    each with half of the head size for P.V; never for other head sizes,
+    several row blocks, or few splits."""
+    rc, info = _lib.attn_plan(1, 8, 2, 4, 6000, 128, 1, 0, 20.0)   # 16 rows, long band
+    assert rc == 0 and info["ncol"] == 2 and info["nsplit"] >= 4, info
+    assert info["workgroups"] == 2 * info["nsplit"] * info["ncol"]
+    rc, info = _lib.attn_plan(8, 32, 8, 1, 8192, 128, 1, 0, 0.0)   # 4 splits: no halves
+    assert rc == 0 and info["ncol"] == 1, info
+    rc, info = _lib.attn_plan(1, 16, 1, 1, 8192, 96, 1, 0, 0.0)    # head size 96: no halves
+    assert rc == 0 and info["ncol"] == 1, info
+    rc, info = _lib.attn_plan(1, 32, 2, 2, 8192, 128, 1, 0, 0.0)   # 32 rows a unit: no halves
+    assert rc == 0 and info["ncol"] == 1, info
+    rc, info = _lib.attn_plan(1, 2, 1, 300, 300, 128, 1, 0, 0.0)   # prefill-like: no halves
+    assert rc == 0 and info["ncol"] == 1, info
