@@ -61,8 +61,9 @@ def test_workload_parity(name):
     assert st["nrmse"] < 1e-2, f"{name}: {st}"
 
 
-# Shapes large enough (>= 512 workgroups) that the plan picks the 8-wave,
-# 256-row prefill blocks -- for head size 128 the variant that fills LDS with
+# Shapes large enough (a workgroup per CU or more) that the plan picks the
+# prefill path -- the 8-wave, 256-row blocks for head sizes other than 128, and
+# for head size 128 the pipelined 4-wave, 128-row kernel that fills LDS with
 # direct global-to-LDS loads -- checked on sampled rows.
 LARGE_BLOCK_CASES = [
     # name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed
