@@ -113,20 +113,24 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   p.rows_per_wg = 16 * p.nqb;
   p.n_pos_blk = (Lq + p.m - 1) / p.m;
   const long long groups = units * p.n_pos_blk;
-  long long ns = 1;
-  int tps = 1 << 30;  // one split: the whole band
-  int ncol = 1;
-  if (groups < kSplitTarget) {
-    // Largest band (in tiles) of any position block (fewer than kSplitTarget blocks here).
+  // Largest band of any position block, in tiles of `keys` keys.
+  auto max_band_tiles = [&](int keys) {
     int max_tiles = 1;
     for (int pb = 0; pb < p.n_pos_blk; ++pb) {
       const int q0 = pb * p.m;
       const int m_eff = Lq - q0 < p.m ? Lq - q0 : p.m;
       int lo, hi;
       block_band(q0, m_eff, Lq, Lkv, causal, window, &lo, &hi);
-      const int tiles = hi / kSplitKeys - lo / kSplitKeys + 1;
+      const int tiles = hi / keys - lo / keys + 1;
       if (tiles > max_tiles) max_tiles = tiles;
     }
+    return max_tiles;
+  };
+  long long ns = 1;
+  int tps = 1 << 30;  // one split: the whole band
+  int ncol = 1;
+  if (groups < kSplitTarget) {
+    const int max_tiles = max_band_tiles(kSplitKeys);
     ns = (kSplitTarget + groups - 1) / groups;
     if (ns > max_tiles) ns = max_tiles;
     // Column halves: with many splits of one 16-row block the last arrival
@@ -142,6 +146,18 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
     }
     tps = (int)((max_tiles + ns - 1) / ns);
     ns = (max_tiles + tps - 1) / tps;
+  }
+  // Wide workgroups: a single 16-row block with a long key range per
+  // workgroup streams 256-key tiles with 8 waves (two per SIMD), twice the
+  // bytes in flight per workgroup, for the same splits.
+  if (p.nqb == 1 && ncol == 1 && (ns > 1 ? tps : max_band_tiles(kSplitKeys)) >= kSplitWideMinTiles) {
+    p.nwaves = kSplitWavesWide;
+    p.keys_per_tile = 32 * kSplitWavesWide;
+    if (ns > 1) {
+      const int max_tiles = max_band_tiles(p.keys_per_tile);
+      tps = (int)((max_tiles + ns - 1) / ns);
+      ns = (max_tiles + tps - 1) / tps;
+    }
   }
   p.nsplit = (int)ns;
   p.tiles_per_split = tps;

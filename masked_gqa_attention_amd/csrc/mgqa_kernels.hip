@@ -1308,21 +1308,25 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the instantiated shapes.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NQB, bool SOFTCAP, int NCOL = 1>
+template <typename T, int DQK, int DV, int NQB, bool SOFTCAP, int NCOL = 1, int NW = kSplitWaves>
 static void launch_split(const dim3& grid, const KernelArgs& args, hipStream_t st) {
-  const dim3 block(64 * kSplitWaves);
+  const dim3 block(64 * NW);
   if (NQB == 1 && args.ring_start >= 0)
-    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, kSplitWaves, SOFTCAP, true, NCOL>), grid, block, 0, st,
-                       args);
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, NW, SOFTCAP, true, NCOL>), grid, block, 0, st, args);
   else
-    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, kSplitWaves, SOFTCAP, false, NCOL>), grid, block, 0, st,
-                       args);
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, NW, SOFTCAP, false, NCOL>), grid, block, 0, st, args);
 }
 
 template <typename T, int DQK, int DV, bool SOFTCAP>
 static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStream_t st) {
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathSplit) {
+    if (plan.nwaves == kSplitWavesWide) {
+      // Eight waves over 256-key tiles: one 16-row block, full width.
+      if (plan.nqb != 1 || plan.ncol != 1) return hipErrorInvalidValue;
+      launch_split<T, DQK, DV, 1, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
+      return hipGetLastError();
+    }
     if (plan.ncol == 2) {
       // Two column halves: each workgroup computes half of P.V's 16-column blocks.
       if constexpr (DV == 8) {

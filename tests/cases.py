@@ -137,6 +137,12 @@ CASES = [
     Case("halves_multitoken_g4_lq4_cap", 1, 8, 2, 4, 6000, 128, causal=True, softcap=20.0, seed=66),
     Case("halves_decode_window_edges", 2, 16, 1, 1, 5000, 128, causal=True, window=1536, seed=67),
     Case("halves_decode_fp16_cap", 1, 32, 2, 1, 4100, 128, causal=True, softcap=40.0, dtype="fp16", seed=68),
+    # one 16-row block and long key ranges per workgroup: 8 waves over 256-key tiles
+    Case("wide_decode_g1_d128", 6, 8, 8, 1, 6000, 128, causal=True, seed=69),
+    Case("wide_decode_nosplit_d72", 64, 64, 8, 1, 3000, 72, causal=True, seed=70),
+    Case("wide_decode_window_cap_fp16", 8, 64, 8, 1, 9000, 128, causal=True, window=5000, softcap=30.0,
+         dtype="fp16", seed=71),
+    Case("wide_multitoken_g2_lq8_d64_cap", 8, 16, 8, 8, 5000, 64, causal=True, softcap=15.0, seed=72),
 ]
 
 CASES_BY_NAME = {c.name: c for c in CASES}

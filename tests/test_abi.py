@@ -205,3 +205,19 @@ def test_column_halves_plan():
     assert rc == 0 and info["ncol"] == 1, info
     rc, info = _lib.attn_plan(1, 2, 1, 300, 300, 128, 1, 0, 0.0)   # prefill-like: no halves
     assert rc == 0 and info["ncol"] == 1, info
+
+
+def test_wide_split_plan():
+    """A single 16-row block with at least eight 128-key tiles per workgroup
+    runs 8 waves over 256-key tiles; few tiles per workgroup, several row
+    blocks or column halves keep 4 waves over 128-key tiles."""
+    rc, info = _lib.attn_plan(8, 32, 8, 1, 8192, 128, 1, 0, 0.0)     # 4 splits of 16 tiles
+    assert rc == 0 and info["keys_per_tile"] == 256 and info["ncol"] == 1, info
+    rc, info = _lib.attn_plan(64, 64, 8, 1, 3000, 72, 1, 0, 0.0)     # no split, 24 tiles
+    assert rc == 0 and info["keys_per_tile"] == 256 and info["nsplit"] == 1, info
+    rc, info = _lib.attn_plan(4, 64, 4, 1, 32768, 128, 1, 4096, 30.0)  # column halves
+    assert rc == 0 and info["keys_per_tile"] == 128 and info["ncol"] == 2, info
+    rc, info = _lib.attn_plan(1, 4, 1, 64, 64, 128, 1, 0, 0.0)         # one tile
+    assert rc == 0 and info["keys_per_tile"] == 128, info
+    rc, info = _lib.attn_plan(1, 16, 16, 729, 729, 72, 0, 0, 0.0)      # 48-row blocks
+    assert rc == 0 and info["keys_per_tile"] == 128, info

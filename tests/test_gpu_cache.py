@@ -122,6 +122,7 @@ RING_CASES = [
     ("ring_multitoken", 1, 8, 2, 4, 600, 600, 599, 256, 0.0),
     ("ring_start0", 2, 4, 1, 1, 513, 513, 0, 0, 10.0),
     ("ring_long_window_halves", 1, 16, 1, 1, 4096, 4096, 1000, 3000, 30.0),
+    ("ring_wide_many_units", 8, 32, 8, 1, 4096, 4096, 1234, 0, 0.0),
 ]
 
 
