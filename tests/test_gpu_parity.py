@@ -66,7 +66,11 @@ def test_determinism_bitwise():
     from masked_gqa_attention_amd import api
     from .cases import CASES_BY_NAME
     from .gpu_util import to_device
-    for name in ("prefill_window_cap_g8", "decode_g16_window_cap", "decode_g4_kv3000"):
+    # one case per kernel form: split (several row blocks, fp16), split with
+    # column halves, wide split, register-staged prefill, pipelined prefill
+    for name in ("prefill_window_cap_g8", "decode_g16_window_cap", "decode_g4_kv3000", "split_nqb3_d72_fp16",
+                 "halves_decode_fp16_cap", "wide_decode_g1_d128", "prefill_big_g16_d96_noncausal",
+                 "prefill_big_g16_d128"):
         c = CASES_BY_NAME[name]
         announce(f"determinism {name}")
         q, k, v = (to_device(a, c.dtype) for a in make_inputs(c))
