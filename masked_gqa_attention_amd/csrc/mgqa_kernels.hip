@@ -1018,12 +1018,14 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 // pairs, head fastest: NQB blocks of 16, m*G <= 16*NQB of them real.  Each
 // 32*NW-key tile is staged once (K and V row-major, V read transposed); wave w
 // takes keys [32w, 32w+32) of it for all rows, so the key axis is split across
-// the waves.  The wave states are merged in LDS in wave order, one 16-row block
-// at a time.  With one split the merged rows are the output; otherwise the
-// split's partial is written and the last split to arrive for the block merges
-// all partials in split order.  With many splits of one 16-row block the key
-// range of a split is shared by two workgroups, each with half of V's columns
-// (DV is then the half's width); each half merges its own partials.
+// the waves.  The wave states are merged in LDS in wave order.  With one
+// split the merged rows are the output; otherwise the split's partial is
+// written and the last split to arrive for the block merges all partials in
+// split order.  NW is 4 (128-key tiles), or 8 (256-key tiles, two waves per
+// SIMD) for a single 16-row block with long key ranges per workgroup.  With
+// many splits of one 16-row block the key range of a split is shared by two
+// workgroups (NCOL = 2), each with half of V's columns (DV is then the half's
+// width); each half merges its own partials.
 // ---------------------------------------------------------------------------
 template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING, int NCOL>
 __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
