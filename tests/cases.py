@@ -143,6 +143,10 @@ CASES = [
     Case("wide_decode_window_cap_fp16", 8, 64, 8, 1, 9000, 128, causal=True, window=5000, softcap=30.0,
          dtype="fp16", seed=71),
     Case("wide_multitoken_g2_lq8_d64_cap", 8, 16, 8, 8, 5000, 64, causal=True, softcap=15.0, seed=72),
+    # head sizes that leave the second column half or the padded tail partly empty
+    Case("halves_decode_d120_cap", 1, 16, 1, 1, 5000, 120, causal=True, softcap=25.0, seed=73),
+    Case("wide_decode_d104", 8, 32, 8, 1, 5000, 104, causal=True, seed=74),
+    Case("wide_decode_d40", 8, 64, 8, 1, 4000, 40, causal=True, window=3000, seed=75),
 ]
 
 CASES_BY_NAME = {c.name: c for c in CASES}
