@@ -1108,10 +1108,11 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   // addresses with the same alignment (which concentrates the first requests
   // on a few memory channels).  The softmax merge is order independent; the
   // order is a fixed function of the shape, so results stay reproducible.
-  // The start is 5*lin modulo the largest power of two <= ntile (a mask, no
-  // division, and always < ntile).
+  // The start is 5*(group, split index) modulo the largest power of two <=
+  // ntile (a mask, no division, and always < ntile): the two column halves of
+  // a key range take the same order, so they read each K tile together.
   const int ntile = max(t1 - t0, 0);
-  const int rot = ntile > 0 ? (int)(((unsigned)lin * 5u) & ((1u << (31 - __builtin_clz((unsigned)ntile))) - 1u)) : 0;
+  const int rot = ntile > 0 ? (int)(((unsigned)lsp * 5u) & ((1u << (31 - __builtin_clz((unsigned)ntile))) - 1u)) : 0;
   auto tile_at = [&](int i) { const int r = i + rot; return t0 + (r >= ntile ? r - ntile : r); };
   if (ntile > 0) {
     fetch_k(tile_at(0) * KEYS);
