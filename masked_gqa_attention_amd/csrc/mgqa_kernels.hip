@@ -1091,18 +1091,30 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   }
   const int t0 = key_lo / KEYS + split * a.tiles_per_split;
   const int t1 = min(key_hi / KEYS + 1, t0 + a.tiles_per_split);
-  RowTile<KEYS, DQK * 4, KP, NT> kt;
-  RowTile<KEYS, DV * 2, VP, NT> vt;
+  // Staging registers for the next tile; with column halves (half-width V
+  // tiles) a second set keeps two tiles in flight.
+  constexpr bool TWO_AHEAD = NCOL == 2;
+  using KTile = RowTile<KEYS, DQK * 4, KP, NT>;
+  using VTile = RowTile<KEYS, DV * 2, VP, NT>;
+  KTile kt, kt2;
+  VTile vt, vt2;
   kt.init(d, tid);
   vt.init(d, tid, col0);
-  auto fetch_k = [&](int k0) {
-    if (RING) kt.load_ring(kg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
-    else kt.load(kg, k0, a.Lkv, d);
+  if constexpr (TWO_AHEAD) {
+    kt2.init(d, tid);
+    vt2.init(d, tid, col0);
+  }
+  auto fetch_into = [&](KTile& ks, VTile& vs, bool k_part, int k0) {
+    if (k_part) {
+      if (RING) ks.load_ring(kg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid);
+      else ks.load(kg, k0, a.Lkv, d);
+    } else {
+      if (RING) vs.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid, col0);
+      else vs.load(vg, k0, a.Lkv, d);
+    }
   };
-  auto fetch_v = [&](int k0) {
-    if (RING) vt.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid, col0);
-    else vt.load(vg, k0, a.Lkv, d);
-  };
+  auto fetch_k = [&](int k0) { fetch_into(kt, vt, true, k0); };
+  auto fetch_v = [&](int k0) { fetch_into(kt, vt, false, k0); };
   // The tiles of the range are visited in a rotated order that differs from
   // workgroup to workgroup, so that the workgroups do not all start on
   // addresses with the same alignment (which concentrates the first requests
@@ -1117,6 +1129,12 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   if (ntile > 0) {
     fetch_k(tile_at(0) * KEYS);
     fetch_v(tile_at(0) * KEYS);
+  }
+  if constexpr (TWO_AHEAD) {
+    if (ntile > 1) {
+      fetch_into(kt2, vt2, true, tile_at(1) * KEYS);
+      fetch_into(kt2, vt2, false, tile_at(1) * KEYS);
+    }
   }
 
   // This lane's rows: column c16 of each 16-row block.
@@ -1142,24 +1160,11 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int it = 0; it < ntile; ++it) {
-    const int t = tile_at(it);
-    const int k0 = t * KEYS;
-    __syncthreads();  // every wave is done with the previous tile
-    // Each half of the staging registers is refilled with the next tile as
-    // soon as it is in LDS, so loads stay in flight while the other half is
-    // written, and the next tile flies during this one.
-    const bool more = it + 1 < ntile;
-    const int kn = more ? tile_at(it + 1) * KEYS : 0;
-    kt.store(Ks, tid);
-    if (more) fetch_k(kn);
-    vt.store(Vs, tid);
-    if (more) fetch_v(kn);
-    __syncthreads();
-    // This wave's 32 keys: skipped when wholly outside the band, unmasked
-    // when wholly inside it.
+  // This wave's 32 keys of the tile at k0: skipped when wholly outside the
+  // band, unmasked when wholly inside it.
+  auto compute = [&](int k0) {
     const int w0 = k0 + 32 * wave;
-    if (w0 > key_hi || w0 + 31 < key_lo) continue;
+    if (w0 > key_hi || w0 + 31 < key_lo) return;
     bool full = w0 + 32 <= a.Lkv;
     if (a.causal) full = full && (w0 + 31 <= pos_min);
     if (a.window > 0) {
@@ -1170,6 +1175,56 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
     else
       tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
+  };
+  if constexpr (TWO_AHEAD) {
+    // Tiles alternate between the two register sets; each set is refilled
+    // with the tile two ahead as soon as it is in LDS.
+    for (int it = 0; it < ntile; it += 2) {
+      __syncthreads();  // every wave is done with the previous tile
+      kt.store(Ks, tid);
+      if (it + 2 < ntile) fetch_into(kt, vt, true, tile_at(it + 2) * KEYS);
+      vt.store(Vs, tid);
+      if (it + 2 < ntile) fetch_into(kt, vt, false, tile_at(it + 2) * KEYS);
+      __syncthreads();
+      compute(tile_at(it) * KEYS);
+      if (it + 1 >= ntile) break;
+      __syncthreads();
+      kt2.store(Ks, tid);
+      if (it + 3 < ntile) fetch_into(kt2, vt2, true, tile_at(it + 3) * KEYS);
+      vt2.store(Vs, tid);
+      if (it + 3 < ntile) fetch_into(kt2, vt2, false, tile_at(it + 3) * KEYS);
+      __syncthreads();
+      compute(tile_at(it + 1) * KEYS);
+    }
+  } else {
+    for (int it = 0; it < ntile; ++it) {
+      const int k0 = tile_at(it) * KEYS;
+      __syncthreads();  // every wave is done with the previous tile
+      // Each half of the staging registers is refilled with the next tile as
+      // soon as it is in LDS, so loads stay in flight while the other half is
+      // written, and the next tile flies during this one.
+      const bool more = it + 1 < ntile;
+      const int kn = more ? tile_at(it + 1) * KEYS : 0;
+      kt.store(Ks, tid);
+      if (more) fetch_k(kn);
+      vt.store(Vs, tid);
+      if (more) fetch_v(kn);
+      __syncthreads();
+      const int w0 = k0 + 32 * wave;
+      if (w0 > key_hi || w0 + 31 < key_lo) continue;
+      bool full = w0 + 32 <= a.Lkv;
+      if (a.causal) full = full && (w0 + 31 <= pos_min);
+      if (a.window > 0) {
+        full = full && (pos_max - w0 < a.window);
+        if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
+      }
+      if (full)
+        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
+                                                           g4);
+      else
+        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
+                                                          g4);
+    }
   }
 
   // ---- merge the wave states (fixed order) ------------------------------------
