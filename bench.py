@@ -208,9 +208,9 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each (batch, kv head) unit is independent; see the sharding note in the design "
-              "document). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each "
+              "(batch, kv head) unit is independent and could run on a GPU of its own). "
+              "Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
