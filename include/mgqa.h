@@ -60,7 +60,10 @@ extern "C" {
 #define MGQA_ERR_WORKSPACE -7  /* workspace missing or smaller than required          */
 #define MGQA_ERR_HIP       -8  /* a HIP runtime call or kernel launch failed          */
 #define MGQA_ERR_DTYPE     -9  /* dtype not MGQA_BF16 / MGQA_FP16                      */
-#define MGQA_ERR_RANGE    -10  /* a size too large for the library's 32-bit indexing  */
+#define MGQA_ERR_RANGE    -10  /* a size too large for the library's 32-bit indexing
+                                  (Lkv*d or S*d above 2^30, Lq*Hq at or above 2^31,
+                                  a tensor above 2^40 elements), or a cache length,
+                                  ring start or append position outside the cache */
 #define MGQA_ERR_UNSUPPORTED -11 /* a valid combination this library does not run      */
 
 #define MGQA_BF16 0

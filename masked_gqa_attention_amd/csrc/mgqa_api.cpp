@@ -24,6 +24,12 @@ constexpr long long kHalfColumnsMinSplits = 8;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Largest K/V unit (one batch row and kv head: Lkv*d or S*d elements).  The
+// kernels address a unit through a buffer descriptor with 32-bit byte offsets
+// and use byte offset 2^31 as "outside every range" (a zero read), so a unit
+// may span at most 2^31 bytes.
+constexpr long long kMaxUnitElems = 1LL << 30;
+
 int validate(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
              float softcap, int dtype) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lkv <= 0 || d <= 0) return MGQA_ERR_SHAPE;
@@ -38,7 +44,7 @@ int validate(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int win
   const long long q_elems = (long long)B * Hq * Lq * d;
   const long long kv_elems = (long long)B * Hkv * Lkv * d;
   if (q_elems > (1LL << 40) || kv_elems > (1LL << 40)) return MGQA_ERR_RANGE;
-  if ((long long)Lkv * d >= (1LL << 31) || (long long)Lq * Hq >= (1LL << 31)) return MGQA_ERR_RANGE;
+  if ((long long)Lkv * d > kMaxUnitElems || (long long)Lq * Hq >= (1LL << 31)) return MGQA_ERR_RANGE;
   return MGQA_OK;
 }
 
@@ -307,7 +313,7 @@ int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void
   if (S <= 0 || length <= 0) return MGQA_ERR_SHAPE;
   if (length > S) return MGQA_ERR_RANGE;
   if (ring_start < -1 || ring_start >= S) return MGQA_ERR_RANGE;
-  if ((long long)S * d >= (1LL << 31)) return MGQA_ERR_RANGE;
+  if ((long long)S * d > kMaxUnitElems) return MGQA_ERR_RANGE;
   Plan p;
   const int err = make_plan(B, Hq, Hkv, Lq, length, d, causal, window, softcap, dtype, &p);
   if (err) return err;

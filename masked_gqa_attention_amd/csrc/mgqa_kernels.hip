@@ -233,6 +233,12 @@ __device__ __forceinline__ void store_row(uint16_t* orow, const f32x4 (&o)[DV], 
 // descriptor based at the tile's first key whose range ends at Lkv, so keys
 // past Lkv read as zero in hardware; chunks past d get an offset beyond any
 // range and read as zero too.  Per-thread offsets are loop invariant.
+//
+// Offsets are unsigned 32-bit bytes.  The front end keeps every (batch, kv
+// head) unit at most 2^30 elements (2^31 bytes), so kOutOfRange, even plus the
+// row steps of a tile, is never inside a descriptor's range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 template <int KEYS, int CH, int PITCH, int NT>
 struct RowTile {
   static constexpr int TOTAL = KEYS * CH;
@@ -242,18 +248,18 @@ struct RowTile {
   static constexpr bool COMPACT = (NT % CH == 0) && (TOTAL % NT == 0);
   static constexpr int NOFF = COMPACT ? 1 : PER;
   u32x4 r[PER];
-  int voff[NOFF];
-  int vstep;  // bytes between consecutive loads of a thread (COMPACT only)
+  uint32_t voff[NOFF];
+  uint32_t vstep;  // bytes between consecutive loads of a thread (COMPACT only)
 
   // col0: first column of the rows this tile holds (a multiple of 8).
   __device__ __forceinline__ void init(int d, int tid, int col0 = 0) {
-    vstep = (NT / CH) * d * 2;
+    vstep = (uint32_t)((NT / CH) * d * 2);
 #pragma unroll
     for (int it = 0; it < NOFF; ++it) {
       const int c = tid + it * NT;
       const int key = c / CH, ch = c % CH;
       const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (col0 + ch * 8 < d);
-      voff[it] = ok ? (key * d + col0 + ch * 8) * 2 : 0x7FFF0000;
+      voff[it] = ok ? (uint32_t)((key * d + col0 + ch * 8) * 2) : kOutOfRange;
     }
   }
   // g: the (batch, kv head) unit's first row; loads keys k0 .. k0+KEYS-1.
@@ -261,8 +267,8 @@ struct RowTile {
     const auto rs = make_rsrc(g + (size_t)k0 * d, (uint32_t)(Lkv - k0) * (uint32_t)d * 2u);
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int vo = COMPACT ? voff[0] + it * vstep : voff[it];
-      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+      const uint32_t vo = COMPACT ? voff[0] + (uint32_t)it * vstep : voff[it];
+      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0));
     }
   }
   // Ring-buffer cache: logical key j of the unit lives in slot
@@ -278,7 +284,7 @@ struct RowTile {
       int slot = ring_start + logical;
       slot -= (slot >= S) ? S : 0;
       const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (logical < Lkv) && (col0 + ch * 8 < d);
-      const uint32_t vo = ok ? (uint32_t)(slot * d + col0 + ch * 8) * 2u : 0x7FFF0000u;
+      const uint32_t vo = ok ? (uint32_t)(slot * d + col0 + ch * 8) * 2u : kOutOfRange;
       r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0));
     }
   }
@@ -851,7 +857,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   auto fetch = [&](int t, int st) {
     // (Forced into scalar registers: the descriptor must be uniform.)
     const int k0 = wave_uniform(t * KEYS);
-    const uint32_t bytes = (uint32_t)wave_uniform((a.Lkv - k0) * (D * 2));
+    const uint32_t bytes = (uint32_t)wave_uniform((int)((uint32_t)(a.Lkv - k0) * (uint32_t)(D * 2)));
     const u32x4 rk = raw_rsrc(kg + (size_t)k0 * D, bytes);
     const u32x4 rv = raw_rsrc(vg + (size_t)k0 * D, bytes);
 #pragma unroll

@@ -126,6 +126,23 @@ def test_attn_fwd_validation_codes():
     assert _lib.attn_fwd(P, P, P, MIS, 1, 4, 1, 64, 64, 128, 1, 0, 0.0, None) == _lib.MGQA_ERR_ALIGN
 
 
+def test_unit_size_limit():
+    # One K/V unit (batch row, kv head) may hold at most 2^30 elements: the
+    # kernels address it with 32-bit byte offsets and keep offset 2^31 for
+    # "outside the range".
+    for d in (128, 120, 64, 8):
+        top = (1 << 30) // d
+        assert _lib.attn_plan(1, 8, 1, 1, top, d, 1, 0, 0.0)[0] == 0
+        assert _lib.attn_plan(1, 8, 1, 1, top + 1, d, 1, 0, 0.0)[0] == _lib.MGQA_ERR_RANGE
+    assert _lib.attn_plan(2, 8, 2, 1, 1 << 23, 128, 0, 0, 0.0)[0] == 0   # many units at the limit
+    f = _lib.attn_fwd_cache
+    ws = ctypes.c_void_p(0x100000)
+    for S, code in (((1 << 23) + 1, _lib.MGQA_ERR_RANGE), (1 << 23, _lib.MGQA_ERR_WORKSPACE)):
+        assert f(P, P, P, P, 1, 16, 1, 1, S, 4096, -1, 128, 1, 0, 0.0, 0, None, 0, None) == code
+    assert f(P, P, P, P, 1, 16, 1, 1, (1 << 23) + 1, 4096, -1, 128, 1, 0, 0.0, 0, ws, 1 << 30,
+             None) == _lib.MGQA_ERR_RANGE
+
+
 def test_non_causal_longer_query_is_allowed_in_plan():
     # No mask and no window: every key is visible to every row, Lq > Lkv is fine.
     rc, info = _lib.attn_plan(1, 2, 1, 100, 10, 64, 0, 0, 0.0)
