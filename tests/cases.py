@@ -147,6 +147,14 @@ CASES = [
     Case("halves_decode_d120_cap", 1, 16, 1, 1, 5000, 120, causal=True, softcap=25.0, seed=73),
     Case("wide_decode_d104", 8, 32, 8, 1, 5000, 104, causal=True, seed=74),
     Case("wide_decode_d40", 8, 64, 8, 1, 4000, 40, causal=True, window=3000, seed=75),
+    # degenerate sizes: one key (the output is that key's value row), one key
+    # for many non-causal rows, a window longer than the sequence (no window),
+    # the largest group with the smallest head size
+    Case("single_key_decode", 1, 4, 1, 1, 1, 128, causal=True, seed=76),
+    Case("single_key_noncausal_longq_d8", 2, 2, 2, 40, 1, 8, seed=77),
+    Case("window_beyond_length_cap", 1, 8, 2, 60, 90, 64, causal=True, window=100000, softcap=10.0,
+         seed=78),
+    Case("max_group_d8_decode", 1, 16, 1, 1, 300, 8, causal=True, seed=79),
 ]
 
 CASES_BY_NAME = {c.name: c for c in CASES}
