@@ -33,8 +33,8 @@ MGQA_FP16 = 1
 MGQA_F32 = 2
 
 # Every symbol the header declares.
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_cache", "kv_cache_append", "attn_workspace_bytes",
-           "attn_plan", "attn_error_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_cache", "attn_fwd_cache_append", "kv_cache_append",
+           "attn_workspace_bytes", "attn_plan", "attn_error_string", "attn_version")
 
 _lib = None
 
@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_ex.restype = i
     lib.attn_fwd_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_fwd_cache.restype = i
+    lib.attn_fwd_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_fwd_cache_append.restype = i
     lib.kv_cache_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp]
     lib.kv_cache_append.restype = i
     lib.attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
@@ -93,6 +95,13 @@ def attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, length, ring_sta
     return load().attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, length, ring_start, d,
                                  int(causal), int(window), float(softcap), int(dtype), workspace,
                                  int(workspace_bytes), stream)
+
+
+def attn_fwd_cache_append(q, k_cache, v_cache, new_k, new_v, out, B, Hq, Hkv, Lq, S, position, d,
+                          causal, window, softcap, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_fwd_cache_append(q, k_cache, v_cache, new_k, new_v, out, B, Hq, Hkv, Lq, S,
+                                        position, d, int(causal), int(window), float(softcap),
+                                        int(dtype), workspace, int(workspace_bytes), stream)
 
 
 def kv_cache_append(k_cache, v_cache, new_k, new_v, B, S, H, D, L, position, cache_dtype, layout,

@@ -166,6 +166,44 @@ def attn_cache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, le
     return out
 
 
+def attn_cache_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      new_k: torch.Tensor, new_v: torch.Tensor, position: int, causal: bool = True,
+                      window: int = 0, softcap: float = 0.0,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """One step over a linear cache: write the Lq new float32 key/value rows
+    new_k, new_v [B,Hkv,Lq,d] into slots position .. position+Lq-1 of the
+    caches [B,Hkv,S,d] (in place, rounded to the cache dtype), then attend
+    with q [B,Hq,Lq,d] (rows at positions position .. position+Lq-1) over
+    keys 0 .. position+Lq-1.  Same result as kv_cache_append followed by
+    attn_cache; on the decode path it is a single kernel launch."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("new_k", new_k),
+                    ("new_v", new_v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype, bfloat16 or float16")
+    if new_k.dtype != torch.float32 or new_v.dtype != torch.float32:
+        raise ValueError("new key/value rows must be float32")
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, S, dk = k_cache.shape
+    if Bk != B or dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape mismatch")
+    if new_k.shape != (B, Hkv, Lq, d) or new_v.shape != new_k.shape:
+        raise ValueError("new rows must be [B, Hkv, Lq, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    nbytes = _lib.attn_workspace_bytes(B, Hq, Hkv, Lq, position + Lq, d, causal, window)
+    ws = _workspace(nbytes, q.device, stream)
+    rc = _lib.attn_fwd_cache_append(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    new_k.data_ptr(), new_v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
+                                    Lq, S, position, d, causal, window, softcap, _DTYPES[q.dtype],
+                                    ws.data_ptr() if ws is not None else None, nbytes, stream)
+    if rc != 0:
+        raise MgqaError(rc, "attn_fwd_cache_append")
+    return out
+
+
 def make_attention(cfg: dict):
     """cfg keys: batch, q_len, kv_len, num_q_heads, num_kv_heads, head_dim,
     causal, window, softcap (seed and name are accepted and ignored: the

@@ -243,7 +243,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 extern "C" {
 
-int attn_version(void) { return 101; }
+int attn_version(void) { return 102; }
 
 const char* attn_error_string(int code) {
   switch (code) {
@@ -328,6 +328,43 @@ int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void
   a.kv_stride = (long long)S * d;
   a.ring_start = ring_start;
   a.ring_slots = S;
+  if (launch(p, a, dtype, softcap > 0.f, stream) != hipSuccess) return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+
+int attn_fwd_cache_append(const void* q, void* k_cache, void* v_cache, const float* new_k,
+                          const float* new_v, void* out, int B, int Hq, int Hkv, int Lq, int S,
+                          int position, int d, int causal, int window, float softcap, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !new_k || !new_v || !out) return MGQA_ERR_NULL;
+  if (S <= 0 || Lq <= 0) return MGQA_ERR_SHAPE;
+  if (position < 0 || Lq > S || position > S - Lq) return MGQA_ERR_RANGE;
+  if ((long long)S * d > kMaxUnitElems) return MGQA_ERR_RANGE;
+  const int length = position + Lq;
+  Plan p;
+  const int err = make_plan(B, Hq, Hkv, Lq, length, d, causal, window, softcap, dtype, &p);
+  if (err) return err;
+  if ((long long)B * Hkv * Lq * d >= (1LL << 31)) return MGQA_ERR_RANGE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(new_k) || !aligned16(new_v))
+    return MGQA_ERR_ALIGN;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return MGQA_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MGQA_ERR_ALIGN;
+  KernelArgs a = make_args(p, q, k_cache, v_cache, out, Hq, Hkv, Lq, length, d, causal, window,
+                           softcap, p.ws_bytes ? workspace : nullptr);
+  a.kv_stride = (long long)S * d;
+  a.ring_slots = S;
+  if (p.path == kPathSplit) {
+    // One launch: the split-KV kernel takes the new keys from the float32
+    // rows and writes them to the caches itself.
+    a.app_k = new_k;
+    a.app_v = new_v;
+    a.app_pos = position;
+    a.app_len = Lq;
+  } else if (launch_append(k_cache, v_cache, new_k, new_v, B, S, Hkv, d, Lq, position, dtype, 1, nullptr,
+                           stream) != hipSuccess) {
+    return MGQA_ERR_HIP;
+  }
   if (launch(p, a, dtype, softcap > 0.f, stream) != hipSuccess) return MGQA_ERR_HIP;
   return MGQA_OK;
 }

@@ -70,6 +70,12 @@ struct KernelArgs {
   int nrows;          // m*G rows of a full position block
   FastDiv div_g, div_hkv, div_npos, div_nsplit;  // for G, Hkv, n_pos_blk, nsplit
   int nwg;            // workgroups of the launch (the grid size, read with the other arguments)
+  // Fused cache append (split path, linear cache): keys app_pos .. app_pos+app_len-1
+  // (one per query position) come from the float32 rows app_k / app_v
+  // ([unit][app_len][d]) and are written to K / V.  app_len 0: no append.
+  const float* app_k;
+  const float* app_v;
+  int app_pos, app_len;
 };
 
 struct Plan {

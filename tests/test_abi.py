@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_version_and_error_strings():
-    assert _lib.attn_version() == 101
+    assert _lib.attn_version() == 102
     for code in range(-11, 1):
         s = _lib.error_string(code)
         assert s and s != "unknown error code"
@@ -107,6 +107,26 @@ def test_cache_entry_point_validation_codes():
     assert call(Lq=64, Hq=4, ring=5) == _lib.MGQA_ERR_UNSUPPORTED  # ring needs the decode path
     assert call() == _lib.MGQA_ERR_WORKSPACE               # split decode without workspace
     assert f(None, P, P, P, 1, 16, 1, 1, 64, 64, -1, 128, 1, 0, 0.0, 0, None, 0, None) == _lib.MGQA_ERR_NULL
+
+
+def test_cache_append_entry_point_validation_codes():
+    f = _lib.attn_fwd_cache_append
+
+    def call(q=P, kc=P, vc=P, nk=P, nv=P, out=P, B=1, Hq=8, Hkv=2, Lq=1, S=4096, pos=100, d=128,
+             causal=1, W=0, cap=0.0, dt=0, ws=None, wsb=0):
+        return f(q, kc, vc, nk, nv, out, B, Hq, Hkv, Lq, S, pos, d, causal, W, cap, dt, ws, wsb, None)
+    assert call(nk=None) == _lib.MGQA_ERR_NULL
+    assert call(nv=None) == _lib.MGQA_ERR_NULL
+    assert call(S=0) == _lib.MGQA_ERR_SHAPE
+    assert call(pos=-1) == _lib.MGQA_ERR_RANGE
+    assert call(pos=4096) == _lib.MGQA_ERR_RANGE             # position + Lq > S
+    assert call(Lq=4, pos=4093) == _lib.MGQA_ERR_RANGE
+    assert call(S=(1 << 23) + 1) == _lib.MGQA_ERR_RANGE      # unit above 2^30 elements
+    assert call(d=100) == _lib.MGQA_ERR_HEAD_DIM
+    assert call(nk=MIS) == _lib.MGQA_ERR_ALIGN
+    assert call(nv=MIS) == _lib.MGQA_ERR_ALIGN
+    assert call(Hkv=8, Hq=32, B=8, pos=8191, S=8192) == _lib.MGQA_ERR_WORKSPACE  # split decode
+    assert call(dt=2) == _lib.MGQA_ERR_DTYPE
 
 
 def test_append_validation_codes():

@@ -6,7 +6,11 @@
 * attention over a cache prefix (strided K/V rows) and over a ring buffer:
   bit-identical to the same attention over contiguous keys, and within the
   task page's tolerance of the float64 oracle;
-* append followed by decode over the filled prefix.
+* append followed by decode over the filled prefix;
+* the fused step (attn_fwd_cache_append): the same output bits and the same
+  cache contents as the update followed by attention over the cache, for the
+  one-launch split-KV plans (4- and 8-wave, column halves, several position
+  blocks, padded head sizes) and the two-launch prefill plans.
 """
 import json
 import os
@@ -177,4 +181,53 @@ def test_append_then_decode():
     vv = want_v.permute(perm)[:, :, :length].float().double().numpy()
     ref = oracle.attention(q.float().double().numpy(), kk, vv, True, 1000, 20.0)
     ok, st = compare(out.float().cpu().double().numpy(), ref)
+    assert ok, st
+
+
+FUSED_CASES = [
+    # name, B, Hq, Hkv, Lq, S, position, d, causal, window, softcap, dtype
+    ("decode_g4", 2, 8, 2, 1, 3000, 2499, 128, True, 0, 0.0, "bf16"),
+    ("decode_g16_window_cap_halves", 1, 16, 1, 1, 6000, 4999, 128, True, 1536, 30.0, "bf16"),
+    ("decode_wide_g1", 6, 8, 8, 1, 7000, 5999, 128, True, 0, 0.0, "bf16"),
+    ("multitoken_g4_tile_edge", 1, 8, 2, 3, 1500, 1278, 128, True, 300, 0.0, "bf16"),
+    ("multitoken_position_blocks_d64", 1, 16, 2, 16, 2100, 2000, 64, True, 0, 0.0, "bf16"),
+    ("fp16_d72_cap", 1, 6, 2, 2, 900, 700, 72, True, 0, 20.0, "fp16"),
+    ("noncausal_window_g2", 1, 4, 2, 4, 800, 500, 128, False, 64, 0.0, "bf16"),
+    ("prefill_pipelined", 4, 64, 8, 512, 1024, 400, 128, True, 100, 0.0, "bf16"),
+    ("prefill_d64", 4, 32, 16, 512, 1200, 600, 64, True, 0, 0.0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: c[0])
+def test_fused_append_matches_update_then_attention(case):
+    from masked_gqa_attention_amd import _lib, api
+    name, B, Hq, Hkv, Lq, S, pos, d, causal, W, cap, dt = case
+    length = pos + Lq
+    rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, length, d, int(causal), W, cap, 0 if dt == "bf16" else 1)
+    assert rc == 0
+    announce(f"fused append {name} {plan}")
+    q = to_device(_rand(500, (B, Hq, Lq, d), dt), dt)
+    kc = to_device(_rand(501, (B, Hkv, S, d), dt), dt)
+    vc = to_device(_rand(502, (B, Hkv, S, d), dt), dt)
+    # The slots about to be written hold NaN: a read of them before the
+    # update would reach the output.
+    kc[:, :, pos:length] = float("nan")
+    vc[:, :, pos:length] = float("nan")
+    rng = np.random.default_rng(503)
+    nk = torch.from_numpy(rng.standard_normal((B, Hkv, Lq, d)).astype(np.float32)).cuda()
+    nv = torch.from_numpy(rng.standard_normal((B, Hkv, Lq, d)).astype(np.float32)).cuda()
+    kc1, vc1, kc2, vc2 = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    got = api.attn_cache_append(q, kc1, vc1, nk, nv, pos, causal=causal, window=W, softcap=cap)
+    assert api.kv_cache_append(kc2, vc2, nk, nv, pos, layout=1) == length
+    want = api.attn_cache(q, kc2, vc2, length, causal=causal, window=W, softcap=cap)
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16)), "K cache differs"
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16)), "V cache differs"
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "output differs"
+    ref = oracle.attention(synth.storage_to_f64(to_host(q, dt), dt),
+                           synth.storage_to_f64(to_host(kc2[:, :, :length].contiguous(), dt), dt),
+                           synth.storage_to_f64(to_host(vc2[:, :, :length].contiguous(), dt), dt),
+                           causal, W, cap)
+    ok, st = compare(synth.storage_to_f64(to_host(got, dt), dt), ref)
+    print(name, st, flush=True)
     assert ok, st
