@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the masked GQA attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workloads a,b] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workloads a,b] [--no-cpu-baseline] [--no-cache-step]
 
 A step is one attention call (one pass of the whole path: band plan, K/V
 staging, Q.K^T, softcap, mask, online softmax, P.V, epilogue, and for decode
@@ -10,6 +10,9 @@ synthetic input already resident in HBM.  The headline workload is the GQA
 4:1 decode over 8192 cached keys (B=8, Hq=32, Hkv=8, d=128), reported in
 GB/s of algorithmic bytes; the other workloads are measured the same way and
 listed under "workloads" (TFLOP/s for prefill/encoder, GB/s for decode).
+The two decode workloads are also timed as a step over a KV cache
+("cache_step": the new rows written by kv_cache_append and then attended by
+attn_fwd_cache, against the one fused attn_fwd_cache_append call).
 
 Timing: W untimed calls, then exactly K calls between two HIP events on the
 stream the kernels run on, bracketed by device synchronisation.  Inputs
@@ -115,6 +118,67 @@ class Runner:
         return synth.storage_to_f64(arr, self.w.dtype)
 
 
+# Decode workloads also timed as a step over a KV cache (new rows written, then attended).
+CACHE_STEP_WORKLOADS = ("decode_gqa4_kv8192", "decode_gqa16_kv32768_w4096_cap30")
+
+
+def cache_step(r, steps, warmup):
+    """A decode step over a KV cache holding the workload's K/V (Lkv slots per
+    batch row and kv head): the Lq new float32 key/value rows are written at
+    position Lkv - Lq and the queries attend over all Lkv keys.  Timed as two
+    calls (kv_cache_append, then attn_fwd_cache) and as the single fused call
+    (attn_fwd_cache_append), on the runner's device copies (the caches), so
+    the same bytes stream from HBM as in the attention-only timing."""
+    import numpy as np
+    from masked_gqa_attention_amd import _lib
+    torch, w = r.torch, r.w
+    lib = _lib.load()
+    rng = np.random.default_rng(w.seed + 7)
+    nk, nv = (torch.from_numpy(rng.standard_normal((w.B, w.Hkv, w.Lq, w.d), dtype=np.float32)).cuda()
+              for _ in range(2))
+    pos = w.Lkv - w.Lq
+    dt = _lib.MGQA_BF16 if w.dtype == "bf16" else _lib.MGQA_FP16
+    ws = r.ws.data_ptr() if r.ws_bytes else None
+    cap = ctypes.c_float(w.softcap)
+    outs = [torch.empty_like(t[0]) for t in r.sets]
+    two, fused = [], []
+    for (tq, tk, tv), to in zip(r.sets, outs):
+        q, kc, vc, o = tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), to.data_ptr()
+        two.append(((kc, vc, nk.data_ptr(), nv.data_ptr(), w.B, w.Lkv, w.Hkv, w.d, w.Lq, pos, dt, 1, None,
+                     r.stream),
+                    (q, kc, vc, o, w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.Lkv, -1, w.d, int(w.causal), w.window,
+                     cap, dt, ws, r.ws_bytes, r.stream)))
+        fused.append((q, kc, vc, nk.data_ptr(), nv.data_ptr(), o, w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, pos, w.d,
+                      int(w.causal), w.window, cap, dt, ws, r.ws_bytes, r.stream))
+
+    def call_two(i):
+        a, b = two[i % len(two)]
+        if lib.kv_cache_append(*a) != 0 or lib.attn_fwd_cache(*b) != 0:
+            raise RuntimeError("cache update or attention failed")
+
+    def call_fused(i):
+        if lib.attn_fwd_cache_append(*fused[i % len(fused)]) != 0:
+            raise RuntimeError("attn_fwd_cache_append failed")
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    t_two, t_fused = timed(call_two), timed(call_fused)
+    fig = figures(w, t_fused)
+    return {"new_rows": w.Lq, "position": pos, "cache_slots": w.Lkv, "steps": steps,
+            "update_then_attention_ms": t_two, "fused_ms": t_fused,
+            "fused_value": fig["value"], "unit": fig["unit"], "fused_frac": fig["frac"]}
+
+
 def copies_for(w) -> int:
     from masked_gqa_attention_amd import accounting
     touched = accounting.workload_work(w)["bytes"]
@@ -202,6 +266,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads to measure besides the headline, or 'all'/'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-step", action="store_true",
+                    help="skip the decode-step-over-a-cache timings (update + attention, fused)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a known-size "
                          "reference for hardware byte counters)")
@@ -250,6 +316,11 @@ def main(argv=None) -> int:
                          "plan": plan, "shape": w.describe()}
         log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
             f"({100 * fig['frac']:.1f}% of {fig['bound']} peak)")
+        if name in CACHE_STEP_WORKLOADS and not args.no_cache_step:
+            st = cache_step(r, steps, warmup)
+            results[name]["cache_step"] = st
+            log(f"{name} as a cache step: update + attention {st['update_then_attention_ms'] * 1e3:.2f} us, "
+                f"fused {st['fused_ms'] * 1e3:.2f} us")
         if name == HEADLINE:
             headline = (r, ms, steps, fig)
         else:
