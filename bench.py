@@ -148,7 +148,7 @@ def cache_step(r, steps, warmup):
                      r.stream),
                     (q, kc, vc, o, w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.Lkv, -1, w.d, int(w.causal), w.window,
                      cap, dt, ws, r.ws_bytes, r.stream)))
-        fused.append((q, kc, vc, nk.data_ptr(), nv.data_ptr(), o, w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, pos, w.d,
+        fused.append((q, kc, vc, nk.data_ptr(), nv.data_ptr(), o, w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, pos, -1, w.d,
                       int(w.causal), w.window, cap, dt, ws, r.ws_bytes, r.stream))
 
     def call_two(i):

@@ -114,30 +114,37 @@ int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void
                    int causal, int window, float softcap, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* One decode (or chunked-prefill) step over a linear KV cache with the cache
- * update folded in: the KV-cache update at a position of the TensorTonic page
- * ("KV Cache Update at a Position") followed by the attention of the task
- * page over the updated cache.  Equivalent to
+/* One decode (or chunked-prefill) step over a KV cache with the cache update
+ * folded in: the KV-cache update at a position of the TensorTonic page ("KV
+ * Cache Update at a Position") followed by the attention of the task page
+ * over the updated cache.  After the call the cache holds length =
+ * position + Lq logical keys; logical key j lives in slot j (ring_start = -1,
+ * linear cache) or in slot (ring_start + j) mod S (ring buffer, as in
+ * attn_fwd_cache).  The Lq new rows are logical keys position ..
+ * position+Lq-1, and the Lq query rows sit at those positions (the
+ * bottom-right alignment).  For a linear cache this equals
  *   kv_cache_append(k_cache, v_cache, new_k, new_v, B, S, Hkv, d, Lq, position,
  *                   dtype, 1, NULL, stream);
  *   attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, position + Lq, -1,
  *                  d, causal, window, softcap, dtype, workspace, workspace_bytes, stream);
- * with the same output bits and the same cache contents afterwards.
- *   q, out      : [B][Hq][Lq][d] of dtype; the Lq query rows sit at key positions
- *                 position .. position+Lq-1 (the bottom-right alignment).
- *   k/v_cache   : [B][Hkv][S][d] of dtype, updated in place: slots
- *                 position .. position+Lq-1 receive new_k / new_v rounded to
- *                 dtype (nearest even); no other slot is written.
+ * with the same output bits and the same cache contents afterwards; for a
+ * ring, the same with the new rows written to their ring slots.
+ *   q, out      : [B][Hq][Lq][d] of dtype.
+ *   k/v_cache   : [B][Hkv][S][d] of dtype, updated in place: the new rows' slots
+ *                 receive new_k / new_v rounded to dtype (nearest even); no
+ *                 other slot is written.
  *   new_k/new_v : float32 [B][Hkv][Lq][d], 16-byte aligned, not overlapping the caches.
- * Requires 0 <= position <= S - Lq (else MGQA_ERR_RANGE).  On the split-KV path
- * (decode, multi-token decode) this is one kernel launch that reads the new
- * keys from new_k / new_v and writes them to the caches itself; otherwise the
- * update kernel runs first on the same stream.  Workspace: attn_workspace_bytes
- * with Lkv = position + Lq.  Other arguments, errors and ownership as attn_fwd_ex. */
+ * Requires 0 <= position <= S - Lq and -1 <= ring_start < S (else
+ * MGQA_ERR_RANGE).  On the split-KV path (decode, multi-token decode) this is
+ * one kernel launch that reads the new keys from new_k / new_v and writes them
+ * to the caches itself; otherwise the update kernel runs first on the same
+ * stream (linear caches only: a ring needs the decode path, Hq/Hkv * Lq <= 16,
+ * else MGQA_ERR_UNSUPPORTED).  Workspace: attn_workspace_bytes with
+ * Lkv = position + Lq.  Other arguments, errors and ownership as attn_fwd_ex. */
 int attn_fwd_cache_append(const void* q, void* k_cache, void* v_cache, const float* new_k,
                           const float* new_v, void* out, int B, int Hq, int Hkv, int Lq, int S,
-                          int position, int d, int causal, int window, float softcap, int dtype,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          int position, int ring_start, int d, int causal, int window, float softcap,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* KV-cache update at a position (TensorTonic, "KV Cache Update at a
  * Position"): for every batch row and head, slots position .. position+L-1 of

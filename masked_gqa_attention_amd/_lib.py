@@ -59,7 +59,8 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_ex.restype = i
     lib.attn_fwd_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_fwd_cache.restype = i
-    lib.attn_fwd_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_fwd_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz,
+                                          vp]
     lib.attn_fwd_cache_append.restype = i
     lib.kv_cache_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp]
     lib.kv_cache_append.restype = i
@@ -97,11 +98,13 @@ def attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, length, ring_sta
                                  int(workspace_bytes), stream)
 
 
-def attn_fwd_cache_append(q, k_cache, v_cache, new_k, new_v, out, B, Hq, Hkv, Lq, S, position, d,
-                          causal, window, softcap, dtype, workspace, workspace_bytes, stream) -> int:
+def attn_fwd_cache_append(q, k_cache, v_cache, new_k, new_v, out, B, Hq, Hkv, Lq, S, position,
+                          ring_start, d, causal, window, softcap, dtype, workspace, workspace_bytes,
+                          stream) -> int:
     return load().attn_fwd_cache_append(q, k_cache, v_cache, new_k, new_v, out, B, Hq, Hkv, Lq, S,
-                                        position, d, int(causal), int(window), float(softcap),
-                                        int(dtype), workspace, int(workspace_bytes), stream)
+                                        position, ring_start, d, int(causal), int(window),
+                                        float(softcap), int(dtype), workspace, int(workspace_bytes),
+                                        stream)
 
 
 def kv_cache_append(k_cache, v_cache, new_k, new_v, B, S, H, D, L, position, cache_dtype, layout,

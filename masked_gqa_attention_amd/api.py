@@ -168,13 +168,14 @@ def attn_cache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, le
 
 def attn_cache_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       new_k: torch.Tensor, new_v: torch.Tensor, position: int, causal: bool = True,
-                      window: int = 0, softcap: float = 0.0,
+                      window: int = 0, softcap: float = 0.0, ring_start: int = -1,
                       out: torch.Tensor | None = None) -> torch.Tensor:
-    """One step over a linear cache: write the Lq new float32 key/value rows
-    new_k, new_v [B,Hkv,Lq,d] into slots position .. position+Lq-1 of the
-    caches [B,Hkv,S,d] (in place, rounded to the cache dtype), then attend
-    with q [B,Hq,Lq,d] (rows at positions position .. position+Lq-1) over
-    keys 0 .. position+Lq-1.  Same result as kv_cache_append followed by
+    """One step over a cache: write the Lq new float32 key/value rows
+    new_k, new_v [B,Hkv,Lq,d] as logical keys position .. position+Lq-1 of
+    the caches [B,Hkv,S,d] (in place, rounded to the cache dtype; slot j, or
+    (ring_start + j) % S for a ring), then attend with q [B,Hq,Lq,d] (rows at
+    positions position .. position+Lq-1) over logical keys 0 .. position+Lq-1.
+    For a linear cache, the same result as kv_cache_append followed by
     attn_cache; on the decode path it is a single kernel launch."""
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("new_k", new_k),
                     ("new_v", new_v)):
@@ -197,7 +198,8 @@ def attn_cache_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     ws = _workspace(nbytes, q.device, stream)
     rc = _lib.attn_fwd_cache_append(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                     new_k.data_ptr(), new_v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
-                                    Lq, S, position, d, causal, window, softcap, _DTYPES[q.dtype],
+                                    Lq, S, position, ring_start, d, causal, window, softcap,
+                                    _DTYPES[q.dtype],
                                     ws.data_ptr() if ws is not None else None, nbytes, stream)
     if rc != 0:
         raise MgqaError(rc, "attn_fwd_cache_append")

@@ -334,16 +334,19 @@ int attn_fwd_cache(const void* q, const void* k_cache, const void* v_cache, void
 
 int attn_fwd_cache_append(const void* q, void* k_cache, void* v_cache, const float* new_k,
                           const float* new_v, void* out, int B, int Hq, int Hkv, int Lq, int S,
-                          int position, int d, int causal, int window, float softcap, int dtype,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          int position, int ring_start, int d, int causal, int window, float softcap,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !new_k || !new_v || !out) return MGQA_ERR_NULL;
   if (S <= 0 || Lq <= 0) return MGQA_ERR_SHAPE;
   if (position < 0 || Lq > S || position > S - Lq) return MGQA_ERR_RANGE;
+  if (ring_start < -1 || ring_start >= S) return MGQA_ERR_RANGE;
   if ((long long)S * d > kMaxUnitElems) return MGQA_ERR_RANGE;
   const int length = position + Lq;
   Plan p;
   const int err = make_plan(B, Hq, Hkv, Lq, length, d, causal, window, softcap, dtype, &p);
   if (err) return err;
+  if (ring_start >= 0 && (p.path != kPathSplit || p.n_pos_blk != 1 || p.nqb != 1))
+    return MGQA_ERR_UNSUPPORTED;
   if ((long long)B * Hkv * Lq * d >= (1LL << 31)) return MGQA_ERR_RANGE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(new_k) || !aligned16(new_v))
@@ -353,6 +356,7 @@ int attn_fwd_cache_append(const void* q, void* k_cache, void* v_cache, const flo
   KernelArgs a = make_args(p, q, k_cache, v_cache, out, Hq, Hkv, Lq, length, d, causal, window,
                            softcap, p.ws_bytes ? workspace : nullptr);
   a.kv_stride = (long long)S * d;
+  a.ring_start = ring_start;
   a.ring_slots = S;
   if (p.path == kPathSplit) {
     // One launch: the split-KV kernel takes the new keys from the float32

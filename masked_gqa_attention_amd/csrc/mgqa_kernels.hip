@@ -290,13 +290,15 @@ struct RowTile {
   }
   // Fused cache append: the chunks of keys app_pos .. app_pos+app_len-1 of the
   // tile at k0 take the float32 rows src ([app_len][d]) rounded to T (nearest
-  // even) instead of what load() fetched; the chunks of the keys whose index
-  // minus app_pos lies in [wlo, whi) are also stored to the cache rows at dst
-  // (the unit's slot 0; nullptr: no stores).  Runs only for tiles that hold
-  // appended keys.
+  // even) instead of what load() / load_ring() fetched; the chunks of the keys
+  // whose index minus app_pos lies in [wlo, whi) are also stored to their
+  // cache slot at dst (the unit's slot 0; nullptr: no stores): slot j, or
+  // (ring_start + j) mod S for a ring.  Runs only for tiles that hold appended
+  // keys.
   template <typename T>
   __device__ __forceinline__ void substitute(const float* src, uint16_t* dst, int k0, int app_pos, int app_len,
-                                             int wlo, int whi, int d, int tid, int col0 = 0) {
+                                             int wlo, int whi, int d, int tid, int ring_start, int S,
+                                             int col0 = 0) {
     // An opaque copy of the thread index: the chunk arithmetic below then
     // cannot be hoisted out of this rarely taken branch into the key loop,
     // where it would hold registers.
@@ -314,7 +316,14 @@ struct RowTile {
         const u32x4 v = {Elem<T>::pack2(lo[0], lo[1]), Elem<T>::pack2(lo[2], lo[3]),
                          Elem<T>::pack2(hi[0], hi[1]), Elem<T>::pack2(hi[2], hi[3])};
         r[it] = v;
-        if (dst && i >= wlo && i < whi) *reinterpret_cast<u32x4*>(dst + (size_t)j * d + col) = v;
+        if (dst && i >= wlo && i < whi) {
+          int slot = j;
+          if (ring_start >= 0) {
+            slot = ring_start + j;
+            slot -= (slot >= S) ? S : 0;
+          }
+          *reinterpret_cast<u32x4*>(dst + (size_t)slot * d + col) = v;
+        }
       }
     }
   }
@@ -1148,21 +1157,20 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       if (RING) vs.load_ring(vg, k0, a.Lkv, d, a.ring_start, a.ring_slots, tid, col0);
       else vs.load(vg, k0, a.Lkv, d);
     }
-    // Fused cache append (linear cache): the appended keys are the last
-    // app_len keys, one per query position, and come from the float32 rows.
-    // The workgroup whose position block holds query position i writes key
-    // app_pos + i to the cache (K by the first column half only, V by each
-    // half for its columns); no workgroup reads those cache rows.
-    if constexpr (!RING) {
-      if (a.app_len > 0 && k0 < a.app_pos + a.app_len && k0 + KEYS > a.app_pos) {
-        const size_t src = (size_t)unit * a.app_len * d;
-        if (k_part)
-          ks.template substitute<T>(a.app_k + src, half == 0 ? const_cast<uint16_t*>(kg) : nullptr, k0, a.app_pos,
-                                    a.app_len, q0, q0 + m_eff, d, tid);
-        else
-          vs.template substitute<T>(a.app_v + src, const_cast<uint16_t*>(vg), k0, a.app_pos, a.app_len, q0,
-                                    q0 + m_eff, d, tid, col0);
-      }
+    // Fused cache append: the appended keys are the last app_len keys, one
+    // per query position, and come from the float32 rows.  The workgroup
+    // whose position block holds query position i writes key app_pos + i to
+    // its cache slot (K by the first column half only, V by each half for its
+    // columns); no workgroup reads those cache slots.
+    if (a.app_len > 0 && k0 < a.app_pos + a.app_len && k0 + KEYS > a.app_pos) {
+      const size_t src = (size_t)unit * a.app_len * d;
+      const int rs = RING ? a.ring_start : -1;
+      if (k_part)
+        ks.template substitute<T>(a.app_k + src, half == 0 ? const_cast<uint16_t*>(kg) : nullptr, k0, a.app_pos,
+                                  a.app_len, q0, q0 + m_eff, d, tid, rs, a.ring_slots);
+      else
+        vs.template substitute<T>(a.app_v + src, const_cast<uint16_t*>(vg), k0, a.app_pos, a.app_len, q0,
+                                  q0 + m_eff, d, tid, rs, a.ring_slots, col0);
     }
   };
   auto fetch_k = [&](int k0) { fetch_into(kt, vt, true, k0); };

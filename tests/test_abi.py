@@ -112,9 +112,10 @@ def test_cache_entry_point_validation_codes():
 def test_cache_append_entry_point_validation_codes():
     f = _lib.attn_fwd_cache_append
 
-    def call(q=P, kc=P, vc=P, nk=P, nv=P, out=P, B=1, Hq=8, Hkv=2, Lq=1, S=4096, pos=100, d=128,
-             causal=1, W=0, cap=0.0, dt=0, ws=None, wsb=0):
-        return f(q, kc, vc, nk, nv, out, B, Hq, Hkv, Lq, S, pos, d, causal, W, cap, dt, ws, wsb, None)
+    def call(q=P, kc=P, vc=P, nk=P, nv=P, out=P, B=1, Hq=8, Hkv=2, Lq=1, S=4096, pos=100, ring=-1,
+             d=128, causal=1, W=0, cap=0.0, dt=0, ws=None, wsb=0):
+        return f(q, kc, vc, nk, nv, out, B, Hq, Hkv, Lq, S, pos, ring, d, causal, W, cap, dt, ws, wsb,
+                 None)
     assert call(nk=None) == _lib.MGQA_ERR_NULL
     assert call(nv=None) == _lib.MGQA_ERR_NULL
     assert call(S=0) == _lib.MGQA_ERR_SHAPE
@@ -127,6 +128,9 @@ def test_cache_append_entry_point_validation_codes():
     assert call(nv=MIS) == _lib.MGQA_ERR_ALIGN
     assert call(Hkv=8, Hq=32, B=8, pos=8191, S=8192) == _lib.MGQA_ERR_WORKSPACE  # split decode
     assert call(dt=2) == _lib.MGQA_ERR_DTYPE
+    assert call(ring=4096) == _lib.MGQA_ERR_RANGE            # ring start outside the cache
+    assert call(ring=-2) == _lib.MGQA_ERR_RANGE
+    assert call(Lq=64, Hq=4, Hkv=4, ring=3, pos=1000) == _lib.MGQA_ERR_UNSUPPORTED  # ring needs decode
 
 
 def test_append_validation_codes():

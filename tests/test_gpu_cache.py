@@ -231,3 +231,54 @@ def test_fused_append_matches_update_then_attention(case):
     ok, st = compare(synth.storage_to_f64(to_host(got, dt), dt), ref)
     print(name, st, flush=True)
     assert ok, st
+
+
+FUSED_RING_CASES = [
+    # name, B, Hq, Hkv, Lq, S, position, ring_start, window, softcap, dtype
+    ("ring_full_wrap_g16_window_cap", 1, 16, 1, 1, 4096, 4095, 1000, 4096, 30.0, "bf16"),
+    ("ring_partial_g4", 2, 8, 2, 1, 3000, 1499, 2990, 0, 0.0, "bf16"),
+    ("ring_multitoken_new_rows_wrap", 1, 4, 2, 4, 600, 592, 5, 300, 0.0, "bf16"),
+    ("ring_halves_fp16", 1, 16, 1, 1, 6000, 5999, 123, 1536, 20.0, "fp16"),
+    ("ring_wide_g1", 6, 8, 8, 1, 7000, 6999, 3500, 0, 0.0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_RING_CASES, ids=lambda c: c[0])
+def test_fused_append_on_ring(case):
+    """The fused step on a ring buffer: the new rows land in slots
+    (ring_start + position + i) mod S, and the output equals the ring
+    attention over the cache updated by plain indexing, bit for bit."""
+    from masked_gqa_attention_amd import _lib, api
+    name, B, Hq, Hkv, Lq, S, pos, r0, W, cap, dt = case
+    length = pos + Lq
+    rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, length, 128, 1, W, cap, 0 if dt == "bf16" else 1)
+    assert rc == 0 and plan["path"] == 1
+    announce(f"fused ring append {name} {plan}")
+    d = 128
+    q = to_device(_rand(510, (B, Hq, Lq, d), dt), dt)
+    kc = to_device(_rand(511, (B, Hkv, S, d), dt), dt)
+    vc = to_device(_rand(512, (B, Hkv, S, d), dt), dt)
+    slots = torch.tensor([(r0 + pos + i) % S for i in range(Lq)], device="cuda")
+    kc[:, :, slots] = float("nan")
+    vc[:, :, slots] = float("nan")
+    rng = np.random.default_rng(513)
+    nk = torch.from_numpy(rng.standard_normal((B, Hkv, Lq, d)).astype(np.float32)).cuda()
+    nv = torch.from_numpy(rng.standard_normal((B, Hkv, Lq, d)).astype(np.float32)).cuda()
+    kc1, vc1, kc2, vc2 = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    got = api.attn_cache_append(q, kc1, vc1, nk, nv, pos, causal=True, window=W, softcap=cap,
+                                ring_start=r0)
+    kc2[:, :, slots] = nk.to(kc2.dtype)
+    vc2[:, :, slots] = nv.to(vc2.dtype)
+    want = api.attn_cache(q, kc2, vc2, length, causal=True, window=W, softcap=cap, ring_start=r0)
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16)), "K cache differs"
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16)), "V cache differs"
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "output differs"
+    logical = [(r0 + j) % S for j in range(length)]
+    ref = oracle.attention(synth.storage_to_f64(to_host(q, dt), dt),
+                           synth.storage_to_f64(to_host(kc2[:, :, logical].contiguous(), dt), dt),
+                           synth.storage_to_f64(to_host(vc2[:, :, logical].contiguous(), dt), dt),
+                           True, W, cap)
+    ok, st = compare(synth.storage_to_f64(to_host(got, dt), dt), ref)
+    print(name, st, flush=True)
+    assert ok, st
