@@ -193,6 +193,9 @@ FUSED_CASES = [
     ("multitoken_position_blocks_d64", 1, 16, 2, 16, 2100, 2000, 64, True, 0, 0.0, "bf16"),
     ("fp16_d72_cap", 1, 6, 2, 2, 900, 700, 72, True, 0, 20.0, "fp16"),
     ("noncausal_window_g2", 1, 4, 2, 4, 800, 500, 128, False, 64, 0.0, "bf16"),
+    ("multitoken_halves_position_blocks", 1, 8, 1, 8, 5200, 5000, 128, True, 0, 0.0, "bf16"),
+    ("halves_d120_cap", 1, 16, 1, 1, 5100, 5000, 120, True, 0, 25.0, "bf16"),
+    ("wide_fp16_window", 8, 64, 8, 1, 9100, 9000, 128, True, 5000, 30.0, "fp16"),
     ("prefill_pipelined", 4, 64, 8, 512, 1024, 400, 128, True, 100, 0.0, "bf16"),
     ("prefill_d64", 4, 32, 16, 512, 1200, 600, 64, True, 0, 0.0, "bf16"),
 ]
