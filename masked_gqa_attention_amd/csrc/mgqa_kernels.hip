@@ -1070,7 +1070,10 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 // SIMD) for a single 16-row block with long key ranges per workgroup.  With
 // many splits of one 16-row block the key range of a split is shared by two
 // workgroups (NCOL = 2), each with half of V's columns (DV is then the half's
-// width); each half merges its own partials.
+// width); each half merges its own partials.  A decode step with the KV-cache
+// update folded in (TensorTonic, "KV Cache Update at a Position") passes the
+// new rows as float32 inputs: the tiles holding them take them from there,
+// and one workgroup per new key writes it to its cache slot.
 // ---------------------------------------------------------------------------
 template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING, int NCOL>
 __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
