@@ -3,8 +3,9 @@
     python -m masked_gqa_attention_amd.build [--verbose]
 
 Every HIP source is compiled for gfx950 only, with packed fp32 instructions
-disabled, and linked into masked_gqa_attention_amd/libmgqa.so next to this
-file.  The build always recompiles (it is the "does it build" check).
+disabled and matrix-core accumulators in architectural registers, and
+linked into masked_gqa_attention_amd/libmgqa.so next to this file.  The
+build always recompiles (it is the "does it build" check).
 """
 from __future__ import annotations
 
@@ -28,6 +29,11 @@ ARCH = "gfx950"
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core instructions take their accumulators in architectural
+    # registers: with the heuristic choice the split-KV kernels kept the
+    # accumulators in accumulation registers and copied them back and forth
+    # on every key tile (same results, 14% slower on the 729-token encoder).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

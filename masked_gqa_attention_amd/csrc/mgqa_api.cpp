@@ -165,6 +165,15 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
       ns = (max_tiles + tps - 1) / tps;
     }
   }
+  // Three 16-row blocks over an unsplit band of at least four 128-key tiles
+  // (head size <= 96; the 729-token encoder): 8 waves over 256-key tiles, so
+  // each SIMD runs two waves with half of the tiles each (encoder 15.0 ->
+  // 13.9 us).  The instance fits 256 registers only with the matrix-core
+  // accumulators in architectural registers (build flag).
+  if (p.nqb == 3 && ns == 1 && p.dv <= kSplitWideMaxDv && max_band_tiles(kSplitKeys) >= kSplitWide3MinTiles) {
+    p.nwaves = kSplitWavesWide;
+    p.keys_per_tile = 32 * kSplitWavesWide;
+  }
   p.nsplit = (int)ns;
   p.tiles_per_split = tps;
   p.ncol = ns > 1 ? ncol : 1;

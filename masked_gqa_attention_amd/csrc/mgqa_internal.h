@@ -19,9 +19,11 @@ constexpr int kPipe4Keys = 32;
 constexpr int kSplitWaves = 4;
 constexpr int kSplitKeys = 32 * kSplitWaves;
 // Wide split workgroups: 8 waves over 256-key tiles, for one 16-row block with
-// a long key range per workgroup (decode).
+// a long key range per workgroup (decode), or three 16-row blocks over a short
+// unsplit key band (encoder-sized sequences).
 constexpr int kSplitWavesWide = 8;
 constexpr int kSplitWideMinTiles = 8;  // 128-key tiles per workgroup from which they are used
+constexpr int kSplitWide3MinTiles = 4; // the same for three 16-row blocks (unsplit bands)
 constexpr int kSplitMaxNqb = 4;     // 16-row blocks per workgroup, head size <= 96
 constexpr int kSplitMaxNqbWide = 2; // head size > 96 (register budget)
 constexpr int kSplitWideMaxDv = 6;  // P.V 16-column blocks up to which 3 and 4 row blocks exist

@@ -383,12 +383,14 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
 // banks.
 
 // One 32-key step: scores, softcap, mask, online softmax and P.V; each
-// fragment is read from LDS right before its products.
+// fragment is read from LDS right before its products.  The MASK instance
+// applies the mask only when rmask is set (a run-time choice between full and
+// partial tiles within one copy of the code).
 template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SOFTCAP, bool MASK>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int kbase, int kglob0,
                                           const u32x4 (&qf)[NQB][DQK], const int (&qpos)[NQB],
                                           float (&m_e)[NQB], float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
-                                          const KernelArgs& a, int c16, int g4) {
+                                          const KernelArgs& a, int c16, int g4, bool rmask = true) {
   // ---- S^T = K Q^T -------------------------------------------------------
   f32x4 s[NQB][2];
 #pragma unroll
@@ -405,10 +407,15 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   }
 
   // ---- softcap, mask, online softmax, P^T ------------------------------------
-  u32x4 pk[NQB];
+  // Row maxima of every row block first; the accumulators are rescaled under
+  // one wave-uniform branch (rows whose maximum did not grow by more than the
+  // slack are multiplied by exactly 1), so the products and exponentials of
+  // all row blocks form one straight-line block.
+  float mxe[NQB];
+  bool grow = false;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    if (MASK) {
+    if (MASK && rmask) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -423,22 +430,30 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][hh][i]);
     mx = col_max(mx);
-    float mxe;
     if (SOFTCAP) {
       // Same formula as the per-score path below, so the row maximum maps to
       // exactly 2^0 before any rescale slack.
-      mxe = (mx == kNegInf) ? kNegInf
-                            : __builtin_fmaf(fast_rcp(fast_exp2(mx * a.gamma) + 1.0f), -2.0f * a.c2, a.c2);
+      mxe[qb] = (mx == kNegInf) ? kNegInf
+                                : __builtin_fmaf(fast_rcp(fast_exp2(mx * a.gamma) + 1.0f), -2.0f * a.c2, a.c2);
     } else {
-      mxe = mx * a.alpha;
+      mxe[qb] = mx * a.alpha;
     }
-    if (mxe > m_e[qb] + kRescaleSlack) {
-      const float f = fast_exp2(m_e[qb] - mxe);  // 0 when m_e was -inf
-      m_e[qb] = mxe;
+    grow = grow || (mxe[qb] > m_e[qb] + kRescaleSlack);
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const bool up = mxe[qb] > m_e[qb] + kRescaleSlack;
+      const float f = up ? fast_exp2(m_e[qb] - mxe[qb]) : 1.0f;  // 0 when m_e was -inf
+      if (up) m_e[qb] = mxe[qb];
       l_p[qb] *= f;
 #pragma unroll
       for (int db = 0; db < DV; ++db) o[qb][db] *= f;
     }
+  }
+  u32x4 pk[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
     const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
     float p[8];
 #pragma unroll
@@ -1234,7 +1249,14 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       full = full && (pos_max - w0 < a.window);
       if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
     }
-    if (full)
+    // With several row blocks, one copy of the step with a run-time mask
+    // flag: separate full and masked copies leave the accumulators in
+    // different registers on the two paths, merged by register moves on
+    // every tile.
+    if constexpr (NQB > 1)
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4,
+                                                        !full);
+    else if (full)
       tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
     else
       tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
@@ -1281,7 +1303,10 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
         full = full && (pos_max - w0 < a.window);
         if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
       }
-      if (full)
+      if constexpr (NQB > 1)  // one copy of the step, as in compute() above
+        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
+                                                          g4, !full);
+      else if (full)
         tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
                                                            g4);
       else
@@ -1443,10 +1468,20 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathSplit) {
     if (plan.nwaves == kSplitWavesWide) {
-      // Eight waves over 256-key tiles: one 16-row block, full width.
-      if (plan.nqb != 1 || plan.ncol != 1) return hipErrorInvalidValue;
-      launch_split<T, DQK, DV, 1, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
-      return hipGetLastError();
+      // Eight waves over 256-key tiles, full width: one 16-row block (long
+      // decode ranges), or three (short unsplit sequences, head size <= 96).
+      if (plan.ncol != 1) return hipErrorInvalidValue;
+      if (plan.nqb == 1) {
+        launch_split<T, DQK, DV, 1, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
+        return hipGetLastError();
+      }
+      if constexpr (DV <= kSplitWideMaxDv) {
+        if (plan.nqb == 3) {
+          launch_split<T, DQK, DV, 3, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
+          return hipGetLastError();
+        }
+      }
+      return hipErrorInvalidValue;
     }
     if (plan.ncol == 2) {
       // Two column halves: each workgroup computes half of P.V's 16-column blocks.

@@ -249,9 +249,10 @@ def test_column_halves_plan():
 
 
 def test_wide_split_plan():
-    """A single 16-row block with at least eight 128-key tiles per workgroup
-    runs 8 waves over 256-key tiles; few tiles per workgroup, several row
-    blocks or column halves keep 4 waves over 128-key tiles."""
+    """A single 16-row block with at least eight 128-key tiles per workgroup,
+    or three 16-row blocks over an unsplit band of at least four, run 8 waves
+    over 256-key tiles; few tiles per workgroup, two or four row blocks or
+    column halves keep 4 waves over 128-key tiles."""
     rc, info = _lib.attn_plan(8, 32, 8, 1, 8192, 128, 1, 0, 0.0)     # 4 splits of 16 tiles
     assert rc == 0 and info["keys_per_tile"] == 256 and info["ncol"] == 1, info
     rc, info = _lib.attn_plan(64, 64, 8, 1, 3000, 72, 1, 0, 0.0)     # no split, 24 tiles
@@ -260,5 +261,11 @@ def test_wide_split_plan():
     assert rc == 0 and info["keys_per_tile"] == 128 and info["ncol"] == 2, info
     rc, info = _lib.attn_plan(1, 4, 1, 64, 64, 128, 1, 0, 0.0)         # one tile
     assert rc == 0 and info["keys_per_tile"] == 128, info
-    rc, info = _lib.attn_plan(1, 16, 16, 729, 729, 72, 0, 0, 0.0)      # 48-row blocks
-    assert rc == 0 and info["keys_per_tile"] == 128, info
+    rc, info = _lib.attn_plan(1, 16, 16, 729, 729, 72, 0, 0, 0.0)      # 48-row blocks, 6 tiles
+    assert rc == 0 and info["keys_per_tile"] == 256 and info["rows_per_wg"] == 48, info
+    rc, info = _lib.attn_plan(5, 16, 16, 190, 190, 72, 0, 0, 0.0)      # 48-row blocks, 2 tiles
+    assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 48, info
+    rc, info = _lib.attn_plan(1, 16, 16, 700, 900, 80, 1, 300, 0.0)    # 32-row blocks
+    assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 32, info
+    rc, info = _lib.attn_plan(1, 48, 16, 729, 729, 40, 1, 0, 0.0)      # 64-row blocks
+    assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 64, info

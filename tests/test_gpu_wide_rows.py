@@ -1,0 +1,89 @@
+"""Split-KV workgroups of three 16-row blocks on eight waves over 256-key
+tiles (unsplit key bands of at least four 128-key tiles, head size <= 96: the
+729-token encoder and shapes like it).  Each case first checks that the plan
+takes that form (48 rows and 256-key tiles per workgroup, no key split), then
+compares every element with the float64 oracle and two runs bit for bit; the
+fused cache step on such a plan must equal the update followed by the
+attention over the cache."""
+import numpy as np
+import pytest
+
+import oracle
+from masked_gqa_attention_amd import synth
+
+from .cases import compare
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no GPU")]
+
+from .gpu_util import announce, run, to_device, to_host  # noqa: E402
+
+# name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed
+CASES = [
+    ("encoder_bf16", 1, 16, 16, 729, 729, 72, False, 0, 0.0, "bf16", 601),
+    ("encoder_fp16", 1, 16, 16, 729, 729, 72, False, 0, 0.0, "fp16", 602),
+    ("d96_causal_softcap_fp16", 1, 16, 16, 729, 729, 96, True, 0, 30.0, "fp16", 603),
+    ("d64_two_sided_window", 2, 8, 8, 729, 729, 64, False, 200, 0.0, "bf16", 604),
+    ("g3_d48_window_bottom_right", 1, 3, 1, 4096, 4500, 48, True, 1000, 0.0, "bf16", 605),
+    ("g3_d48_window_softcap_fp16", 1, 3, 1, 4096, 4500, 48, True, 1000, 20.0, "fp16", 606),
+]
+
+
+def _plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dt):
+    from masked_gqa_attention_amd import _lib
+    rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), window, softcap, 0 if dt == "bf16" else 1)
+    assert rc == 0
+    assert plan["path"] == 1 and plan["rows_per_wg"] == 48 and plan["keys_per_tile"] == 256, plan
+    assert plan["nsplit"] == 1, plan
+    return plan
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_wide_three_blocks(case):
+    name, B, Hq, Hkv, Lq, Lkv, d, causal, window, cap, dt, seed = case
+    plan = _plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, cap, dt)
+    announce(f"wide 3-block {name} {plan}")
+    q = synth.draw_array(seed, (B, Hq, Lq, d), dt)
+    k = synth.draw_array(seed + 1000, (B, Hkv, Lkv, d), dt)
+    v = synth.draw_array(seed + 2000, (B, Hkv, Lkv, d), dt)
+    got = run(q, k, v, dt, causal, window, cap)
+    again = run(q, k, v, dt, causal, window, cap)
+    assert np.array_equal(got, again), "output differs between two runs"
+    ref = oracle.attention(*(synth.storage_to_f64(a, dt) for a in (q, k, v)), causal, window, cap)
+    ok, st = compare(got, ref)
+    print(name, st, flush=True)
+    assert ok, f"{name}: {st}"
+
+
+def test_wide_three_blocks_fused_cache_step():
+    from masked_gqa_attention_amd import api
+    B, Hq, Hkv, Lq, S, pos, d, dt = 32, 32, 8, 12, 800, 688, 64, "bf16"
+    length = pos + Lq
+    plan = _plan(B, Hq, Hkv, Lq, length, d, True, 0, 0.0, dt)
+    announce(f"wide 3-block fused cache step {plan}")
+    q = to_device(synth.draw_array(611, (B, Hq, Lq, d), dt), dt)
+    kc = to_device(synth.draw_array(612, (B, Hkv, S, d), dt), dt)
+    vc = to_device(synth.draw_array(613, (B, Hkv, S, d), dt), dt)
+    kc[:, :, pos:length] = float("nan")  # a read of a slot before its update would reach the output
+    vc[:, :, pos:length] = float("nan")
+    rng = np.random.default_rng(614)
+    nk = torch.from_numpy(rng.standard_normal((B, Hkv, Lq, d)).astype(np.float32)).cuda()
+    nv = torch.from_numpy(rng.standard_normal((B, Hkv, Lq, d)).astype(np.float32)).cuda()
+    kc1, vc1, kc2, vc2 = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    got = api.attn_cache_append(q, kc1, vc1, nk, nv, pos, causal=True)
+    assert api.kv_cache_append(kc2, vc2, nk, nv, pos, layout=1) == length
+    want = api.attn_cache(q, kc2, vc2, length, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16)), "K cache differs"
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16)), "V cache differs"
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "output differs"
+    ref = oracle.attention(synth.storage_to_f64(to_host(q, dt), dt),
+                           synth.storage_to_f64(to_host(kc2[:, :, :length].contiguous(), dt), dt),
+                           synth.storage_to_f64(to_host(vc2[:, :, :length].contiguous(), dt), dt),
+                           True, 0, 0.0)
+    ok, st = compare(synth.storage_to_f64(to_host(got, dt), dt), ref)
+    print("fused", st, flush=True)
+    assert ok, st
