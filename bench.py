@@ -15,7 +15,10 @@ The two decode workloads are also timed as a step over a KV cache
 attn_fwd_cache, against the one fused attn_fwd_cache_append call).
 
 Timing: W untimed calls, then exactly K calls between two HIP events on the
-stream the kernels run on, bracketed by device synchronisation.  Inputs
+stream the kernels run on, bracketed by device synchronisation; that rate is
+the reported value.  Each workload is then also timed in 30 rounds of at
+least 1 ms of back-to-back calls ("spread": median, 10th and 90th percentile
+of the per-call time over the rounds).  Inputs
 rotate over several copies so that repeated calls stream from HBM rather than
 from the 256 MB last-level cache.  Prints ONE JSON line.
 """
@@ -106,6 +109,28 @@ class Runner:
         end.record()
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps  # ms per call
+
+    def spread(self, ms_est, rounds=30, min_round_ms=1.0):
+        """Per-call time over `rounds` rounds of back-to-back calls, each round
+        at least `min_round_ms` long and timed by its own pair of HIP events
+        on the launch stream: median, 10th and 90th percentile."""
+        torch = self.torch
+        n = max(1, int(-(-min_round_ms // max(ms_est, 1e-6))))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(rounds)]
+        torch.cuda.synchronize()
+        i = 0
+        for a, b in ev:
+            a.record()
+            for _ in range(n):
+                self.call(i)
+                i += 1
+            b.record()
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) / n for a, b in ev)
+        pct = lambda f: per[min(rounds - 1, int(round(f * (rounds - 1))))]
+        return {"rounds": rounds, "calls_per_round": n,
+                "p10_ms": pct(0.1), "median_ms": pct(0.5), "p90_ms": pct(0.9)}
 
     def output_f64(self, i=0):
         from masked_gqa_attention_amd import synth
@@ -311,11 +336,13 @@ def main(argv=None) -> int:
         fig = figures(w, ms)
         rc, plan = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
                                   w.softcap, 0 if w.dtype == "bf16" else 1)
+        sp = r.spread(ms)
         results[name] = {"ms": ms, "steps": steps, "copies": copies, **fig,
-                         "kernel": kernel_name(plan, w),
+                         "kernel": kernel_name(plan, w), "spread": sp,
                          "plan": plan, "shape": w.describe()}
         log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
-            f"({100 * fig['frac']:.1f}% of {fig['bound']} peak)")
+            f"({100 * fig['frac']:.1f}% of {fig['bound']} peak); rounds: median "
+            f"{sp['median_ms'] * 1e3:.2f} us, p10 {sp['p10_ms'] * 1e3:.2f}, p90 {sp['p90_ms'] * 1e3:.2f}")
         if name in CACHE_STEP_WORKLOADS and not args.no_cache_step:
             st = cache_step(r, steps, warmup)
             results[name]["cache_step"] = st
