@@ -1392,56 +1392,65 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   if (!last_flag) return;
 
   // ---- last arrival: merge all splits in split order ---------------------------------
-  // Online merge over groups of 16 splits; every load of a group is issued
-  // before any of them is used.
-  constexpr int CHUNK = 16;
+  // Online merge over groups of CHUNK splits (4, 8 or 16: the smallest that
+  // holds every split when there are at most 16, so no load repeats a split);
+  // every load of a group is issued before any of them is used.
   constexpr int JM = (16 * NQB * CPR + NT - 1) / NT;
   const int nch = nrows * CPR;
   const int base = grp * a.nsplit * rstride;                   // O rows of split 0
   const int base_ml = (grp * NCOL + half) * a.nsplit * rstride;  // (max, sum) of split 0
+  auto merge_splits = [&](auto chunk_tag) {
+    constexpr int CHUNK = decltype(chunk_tag)::value;
 #pragma unroll
-  for (int j = 0; j < JM; ++j) {
-    const int q = tid + j * NT;
-    if (q >= nch) continue;
-    const int row = q / CPR, c4 = q % CPR;
-    float Mg = kNegInf, Lg = 0.f;
-    f32x4 og4 = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.nsplit; s0 += CHUNK) {
-      f32x2 ml[CHUNK];
-      f32x4 x[CHUNK];
+    for (int j = 0; j < JM; ++j) {
+      const int q = tid + j * NT;
+      if (q >= nch) continue;
+      const int row = q / CPR, c4 = q % CPR;
+      float Mg = kNegInf, Lg = 0.f;
+      f32x4 og4 = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < a.nsplit; s0 += CHUNK) {
+        f32x2 ml[CHUNK];
+        f32x4 x[CHUNK];
 #pragma unroll
-      for (int jj = 0; jj < CHUNK; ++jj) {
-        const int sp = min(s0 + jj, a.nsplit - 1);
-        ml[jj] = ld_dev8(rs_ml, (base_ml + sp * rstride + row) * 8);
-        x[jj] = ld_dev16(rs_o, ((base + sp * rstride + row) * dvw + col0 + 4 * c4) * 4);
+        for (int jj = 0; jj < CHUNK; ++jj) {
+          const int sp = min(s0 + jj, a.nsplit - 1);
+          ml[jj] = ld_dev8(rs_ml, (base_ml + sp * rstride + row) * 8);
+          x[jj] = ld_dev16(rs_o, ((base + sp * rstride + row) * dvw + col0 + 4 * c4) * 4);
+        }
+        float mc = Mg;
+#pragma unroll
+        for (int jj = 0; jj < CHUNK; ++jj)
+          if (s0 + jj < a.nsplit) mc = fmaxf(mc, ml[jj][0]);
+        // No branch here, so the compiler can keep all loads of a group in flight.
+        const bool any = mc != kNegInf;
+        const float fr = any ? fast_exp2(Mg - mc) : 1.f;  // 0 while nothing was merged yet
+        Lg *= fr;
+        og4 *= fr;
+        Mg = any ? mc : Mg;
+#pragma unroll
+        for (int jj = 0; jj < CHUNK; ++jj) {
+          const float f =
+              (s0 + jj < a.nsplit && ml[jj][0] != kNegInf) ? fast_exp2(ml[jj][0] - Mg) : 0.f;
+          Lg += f * ml[jj][1];
+          og4 += f * x[jj];
+        }
       }
-      float mc = Mg;
-#pragma unroll
-      for (int jj = 0; jj < CHUNK; ++jj)
-        if (s0 + jj < a.nsplit) mc = fmaxf(mc, ml[jj][0]);
-      // No branch here, so the compiler can keep all loads of a group in flight.
-      const bool any = mc != kNegInf;
-      const float fr = any ? fast_exp2(Mg - mc) : 1.f;  // 0 while nothing was merged yet
-      Lg *= fr;
-      og4 *= fr;
-      Mg = any ? mc : Mg;
-#pragma unroll
-      for (int jj = 0; jj < CHUNK; ++jj) {
-        const float f =
-            (s0 + jj < a.nsplit && ml[jj][0] != kNegInf) ? fast_exp2(ml[jj][0] - Mg) : 0.f;
-        Lg += f * ml[jj][1];
-        og4 += f * x[jj];
+      if (col0 + 4 * c4 < d) {
+        const float inv = 1.0f / Lg;
+        const int pr = fdiv(row, a.div_g);
+        const size_t oo =
+            (((size_t)b * a.Hq + kvh * G + (row - pr * G)) * a.Lq + q0 + pr) * d + col0 + 4 * c4;
+        *reinterpret_cast<u32x2*>(og + oo) =
+            u32x2{Elem<T>::pack2(og4[0] * inv, og4[1] * inv), Elem<T>::pack2(og4[2] * inv, og4[3] * inv)};
       }
     }
-    if (col0 + 4 * c4 < d) {
-      const float inv = 1.0f / Lg;
-      const int pr = fdiv(row, a.div_g);
-      const size_t oo =
-          (((size_t)b * a.Hq + kvh * G + (row - pr * G)) * a.Lq + q0 + pr) * d + col0 + 4 * c4;
-      *reinterpret_cast<u32x2*>(og + oo) =
-          u32x2{Elem<T>::pack2(og4[0] * inv, og4[1] * inv), Elem<T>::pack2(og4[2] * inv, og4[3] * inv)};
-    }
-  }
+  };
+  if (a.nsplit <= 4)
+    merge_splits(std::integral_constant<int, 4>{});
+  else if (a.nsplit <= 8)
+    merge_splits(std::integral_constant<int, 8>{});
+  else
+    merge_splits(std::integral_constant<int, 16>{});
   if (tid == 0)
     __hip_atomic_store(a.ws_cnt + grp * NCOL + half, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
