@@ -10,6 +10,9 @@ synthetic input already resident in HBM.  The headline workload is the GQA
 4:1 decode over 8192 cached keys (B=8, Hq=32, Hkv=8, d=128), reported in
 GB/s of algorithmic bytes; the other workloads are measured the same way and
 listed under "workloads" (TFLOP/s for prefill/encoder, GB/s for decode).
+Three extension shapes are measured the same way under "next_rows": a
+multi-token decode, an encoder with few heads (key splits) and the long
+windowed decode over a ring-buffer cache.
 The two decode workloads are also timed as a step over a KV cache
 ("cache_step": the new rows written by kv_cache_append and then attended by
 attn_fwd_cache, against the one fused attn_fwd_cache_append call).
@@ -141,6 +144,29 @@ class Runner:
         else:
             arr = o.cpu().numpy()
         return synth.storage_to_f64(arr, self.w.dtype)
+
+
+class RingRunner(Runner):
+    """A decode over a ring-buffer KV cache of Lkv slots holding Lkv logical
+    keys (logical key j in slot (RING_START + j) mod Lkv), through
+    attn_fwd_cache; the copies rotate like Runner's."""
+
+    def __init__(self, w, copies):
+        super().__init__(w, copies)
+        from masked_gqa_attention_amd import _lib, synth
+        self.fn = _lib.load().attn_fwd_cache
+        dtype_code = _lib.MGQA_BF16 if w.dtype == "bf16" else _lib.MGQA_FP16
+        self.args = [(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), to.data_ptr(),
+                      w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.Lkv, synth.RING_START, w.d, int(w.causal),
+                      w.window, ctypes.c_float(w.softcap), dtype_code,
+                      self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, self.stream)
+                     for (tq, tk, tv), to in zip(self.sets, self.outs)]
+
+    def call(self, i):
+        rc = self.fn(*self.args[i % len(self.args)])
+        if rc != 0:
+            from masked_gqa_attention_amd import _lib
+            raise RuntimeError(f"attn_fwd_cache failed: {_lib.error_string(rc)}")
 
 
 # Decode workloads also timed as a step over a KV cache (new rows written, then attended).
@@ -293,6 +319,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-step", action="store_true",
                     help="skip the decode-step-over-a-cache timings (update + attention, fused)")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the extension shapes (multi-token decode, few-head split-K encoder, "
+                         "ring-buffer decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a known-size "
                          "reference for hardware byte counters)")
@@ -354,6 +383,30 @@ def main(argv=None) -> int:
             del r
             torch.cuda.empty_cache()
 
+    if not args.no_next_rows and args.workloads == "all":
+        line_next = {}
+        for name, w in synth.NEXT_WORKLOADS.items():
+            copies = copies_for(w)
+            r = (RingRunner if name.startswith("ring_") else Runner)(w, copies)
+            r.call(0)
+            torch.cuda.synchronize()
+            est = r.time(3, 1)
+            steps = int(max(10, min(2000, 200.0 / max(est, 1e-3))))
+            ms = r.time(steps, max(3, steps // 10))
+            fig = figures(w, ms)
+            sp = r.spread(ms)
+            rc, plan = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
+                                      w.softcap, 0 if w.dtype == "bf16" else 1)
+            line_next[name] = {"ms": ms, "steps": steps, "copies": copies, **fig,
+                               "kernel": kernel_name(plan, w), "spread": sp, "plan": plan}
+            log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
+                f"({100 * fig['frac']:.1f}% of {fig['bound']} peak)")
+            del r
+            torch.cuda.empty_cache()
+        results_next = line_next
+    else:
+        results_next = None
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -390,6 +443,7 @@ def main(argv=None) -> int:
                      "alg_bytes_per_launch": fig["alg_bytes"]},
         "workloads": {n: {k: v for k, v in res.items() if k not in ("shape",)}
                       for n, res in results.items()},
+        "next_rows": results_next,
         "device": torch.cuda.get_device_name(0),
         "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
         "torch": torch.__version__,

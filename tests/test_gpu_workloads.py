@@ -102,3 +102,35 @@ def test_large_block_parity(case):
     print(name, st, flush=True)
     assert ok, f"{name}: {st}"
     assert st["nrmse"] < 1e-2, f"{name}: {st}"
+
+
+@pytest.mark.parametrize("name", list(synth.NEXT_WORKLOADS))
+def test_next_workload_parity(name):
+    """The extension shapes the benchmark also times, at their full sizes and
+    through the same entry points: the ring-buffer decode through
+    attn_fwd_cache with the ring start the benchmark uses (the oracle sees
+    the keys in logical order), the others through attn_fwd_ex."""
+    from masked_gqa_attention_amd import api
+    from .gpu_util import to_device, to_host
+    w = synth.NEXT_WORKLOADS[name]
+    announce(f"extension workload {name}")
+    q, k, v = synth.draw_qkv(w)
+    if name.startswith("ring_"):
+        # logical key j lives in slot (RING_START + j) mod S
+        slots = (synth.RING_START + np.arange(w.Lkv)) % w.Lkv
+        kr, vr = np.empty_like(k), np.empty_like(v)
+        kr[:, :, slots] = k
+        vr[:, :, slots] = v
+        tq, tk, tv = (to_device(a, w.dtype) for a in (q, kr, vr))
+        out = api.attn_cache(tq, tk, tv, w.Lkv, causal=w.causal, window=w.window, softcap=w.softcap,
+                             ring_start=synth.RING_START)
+        torch.cuda.synchronize()
+        got = synth.storage_to_f64(to_host(out, w.dtype), w.dtype)
+    else:
+        got = run(q, k, v, w.dtype, w.causal, w.window, w.softcap)
+    ref = oracle.attention(*(synth.storage_to_f64(a, w.dtype) for a in (q, k, v)),
+                           w.causal, w.window, w.softcap)
+    ok, st = compare(got, ref)
+    print(name, st, flush=True)
+    assert ok, f"{name}: {st}"
+    assert st["nrmse"] < 1e-2, f"{name}: {st}"
