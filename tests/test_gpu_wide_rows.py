@@ -87,3 +87,38 @@ def test_wide_three_blocks_fused_cache_step():
     ok, st = compare(synth.storage_to_f64(to_host(got, dt), dt), ref)
     print("fused", st, flush=True)
     assert ok, st
+
+
+# Hot queries (scores spread over tens of units) make the running maximum grow
+# tile after tile, so the rescale of the accumulators (one wave-uniform branch
+# for all row blocks, rows that need none multiplied by exactly 1) is taken
+# often.  Plans with two, three (4- and 8-wave) and four row blocks.
+# name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, qscale, rows, keys_per_tile
+HOT_CASES = [
+    ("hot_3blocks_8waves", 1, 16, 16, 729, 729, 72, False, 0, 0.0, "fp16", 6.0, 48, 256),
+    ("hot_3blocks_8waves_cap", 1, 16, 16, 729, 729, 72, False, 0, 30.0, "bf16", 12.0, 48, 256),
+    ("hot_3blocks_4waves", 5, 16, 16, 190, 190, 72, False, 0, 0.0, "bf16", 12.0, 48, 128),
+    ("hot_2blocks_window", 1, 16, 16, 700, 900, 80, True, 300, 0.0, "bf16", 12.0, 32, 128),
+    ("hot_4blocks_g3", 1, 48, 16, 729, 729, 40, True, 0, 0.0, "fp16", 5.0, 64, 128),
+]
+
+
+@pytest.mark.parametrize("case", HOT_CASES, ids=lambda c: c[0])
+def test_hot_queries_on_row_blocks(case):
+    from masked_gqa_attention_amd import _lib
+    name, B, Hq, Hkv, Lq, Lkv, d, causal, window, cap, dt, qscale, rows, kpt = case
+    rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), window, cap, 0 if dt == "bf16" else 1)
+    assert rc == 0 and plan["path"] == 1 and plan["rows_per_wg"] == rows and plan["keys_per_tile"] == kpt, plan
+    announce(f"hot row blocks {name} {plan}")
+    seed = 700 + len(name)
+    q = synth.draw_array(seed, (B, Hq, Lq, d), dt)
+    q = synth.f32_to_storage((synth.storage_to_f64(q, dt) * qscale).astype(np.float32), dt)
+    k = synth.draw_array(seed + 1, (B, Hkv, Lkv, d), dt)
+    v = synth.draw_array(seed + 2, (B, Hkv, Lkv, d), dt)
+    got = run(q, k, v, dt, causal, window, cap)
+    again = run(q, k, v, dt, causal, window, cap)
+    assert np.array_equal(got, again), "output differs between two runs"
+    ref = oracle.attention(*(synth.storage_to_f64(a, dt) for a in (q, k, v)), causal, window, cap)
+    ok, st = compare(got, ref)
+    print(name, st, flush=True)
+    assert ok, f"{name}: {st}"
