@@ -1082,7 +1082,8 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 // split the merged rows are the output; otherwise the split's partial is
 // written and the last split to arrive for the block merges all partials in
 // split order.  NW is 4 (128-key tiles), or 8 (256-key tiles, two waves per
-// SIMD) for a single 16-row block with long key ranges per workgroup.  With
+// SIMD) for a single 16-row block with long key ranges per workgroup and for
+// three 16-row blocks over an unsplit band of four or more 128-key tiles.  With
 // many splits of one 16-row block the key range of a split is shared by two
 // workgroups (NCOL = 2), each with half of V's columns (DV is then the half's
 // width); each half merges its own partials.  A decode step with the KV-cache
