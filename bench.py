@@ -19,7 +19,11 @@ attn_fwd_cache, against the one fused attn_fwd_cache_append call).
 
 Timing: W untimed calls, then exactly K calls between two HIP events on the
 stream the kernels run on, bracketed by device synchronisation; that rate is
-the reported value.  Each workload is then also timed in 30 rounds of at
+the reported value.  Each workload's record also holds its error against the
+float64 oracle on every output element (max abs/rel error, allclose at
+rtol = atol = 2e-2), whether three calls on the same input gave the same
+bytes, and the oracle's own time on this host's cores (a process pool with
+one worker per core of the affinity mask, started before the GPU is used).  Each workload is then also timed in 30 rounds of at
 least 1 ms of back-to-back calls ("spread": median, 10th and 90th percentile
 of the per-call time over the rounds).  Inputs
 rotate over several copies so that repeated calls stream from HBM rather than
@@ -32,8 +36,10 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
-import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -231,9 +237,11 @@ def cache_step(r, steps, warmup):
 
 
 def copies_for(w) -> int:
+    """Input copies rotated through so that they total at least twice the
+    last-level cache (never fewer than three)."""
     from masked_gqa_attention_amd import accounting
     touched = accounting.workload_work(w)["bytes"]
-    return max(2, min(32, -(-2 * LLC_BYTES // max(touched, 1))))
+    return max(3, min(32, -(-2 * LLC_BYTES // max(touched, 1))))
 
 
 def figures(w, ms):
@@ -253,45 +261,90 @@ def kernel_name(plan, w) -> str:
     """The attention kernel a plan launches (as in the library's dispatch)."""
     if plan.get("path") == 1:
         return "splitkv_kernel"
+    if plan.get("path") == 2:
+        return "encoder_kernel"
     return "prefill_pipe4_kernel" if w.d == 128 else "prefill_kernel"
 
 
-def blas_threads() -> int:
+def blas_config() -> str:
+    """One line naming numpy's BLAS (the oracle's matrix products)."""
     try:
-        from threadpoolctl import threadpool_info
-        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-        return max(n) if n else 1
+        cfg = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{cfg.get('name')} {cfg.get('version')}"
     except Exception:  # pragma: no cover
-        return 1
+        return "unknown"
 
 
-def cpu_baseline(runner, gpu_out):
-    """The float64 oracle, as it stands, on the headline workload's input
-    (all rows), timed on this host; also the GPU output's error against it."""
-    import numpy as np
-    import oracle
+def determinism(r) -> bool:
+    """Three calls on the first input copy give the same output bytes."""
+    torch = r.torch
+    outs = []
+    for _ in range(3):
+        r.call(0)
+        torch.cuda.synchronize()
+        outs.append(r.outs[0].view(torch.int16).clone())
+    return all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def oracle_leg(pool, w, host, gpu_out, runs):
+    """The float64 oracle, as it stands, on the workload's whole input, run
+    head by head in the process pool: its wall time (median of `runs`) in the
+    workload's algorithmic unit, and the GPU output's error against it on
+    every element."""
     from masked_gqa_attention_amd import accounting, synth
-    w = runner.w
-    q, k, v = runner.host
-    qf, kf, vf = (synth.storage_to_f64(a, w.dtype) for a in (q, k, v))
-    times = []
-    t_total = time.perf_counter()
-    ref = None
-    # Repeat the whole-input oracle until about 10 s of CPU work (3 runs at least).
-    while len(times) < 3 or (time.perf_counter() - t_total) < 10.0:
-        t0 = time.perf_counter()
-        ref = oracle.attention(qf, kf, vf, w.causal, w.window, w.softcap)
-        times.append(time.perf_counter() - t0)
+    qf, kf, vf = (synth.storage_to_f64(a, w.dtype) for a in host)
+    times, ref = [], None
+    for _ in range(runs):
+        ref, t = pool.timed_attention(qf, kf, vf, w.causal, w.window, w.softcap)
+        times.append(t)
     t = sorted(times)[len(times) // 2]
     wk = accounting.workload_work(w)
+    decode = w.Lq * w.G <= 16
     err = np.abs(gpu_out - ref)
-    ok = bool(np.isfinite(gpu_out).all() and (err <= 2e-2 + 2e-2 * np.abs(ref)).all())
+    finite = bool(np.isfinite(gpu_out).all())
     return {
-        "value": wk["bytes"] / t / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-        "sample": f"whole {w.name} input ({w.B * w.Hq * w.Lq} query rows x {w.Lkv} keys), "
-                  f"median of {len(times)} runs of {t:.3f} s ({time.perf_counter() - t_total:.1f} s in all)",
-        "seconds": t, "parity_vs_gpu": {"ok": ok, "max_abs_err": float(err.max())},
+        "oracle": {"value": (wk["bytes"] / t / 1e9) if decode else (wk["flops"] / t / 1e9),
+                   "unit": "GB/s" if decode else "GFLOP/s", "seconds": t, "runs": runs,
+                   "cores": pool.workers, "kind": "oracle"},
+        "parity": {"elements": int(gpu_out.size), "max_abs_err": float(err.max()),
+                   "max_rel_err": float((err / np.maximum(np.abs(ref), 1e-6)).max()),
+                   "nrmse": float(np.sqrt(np.mean(err ** 2)) / (np.sqrt(np.mean(ref ** 2)) or 1.0)),
+                   "allclose": finite and bool((err <= 2e-2 + 2e-2 * np.abs(ref)).all()),
+                   "rtol": 2e-2, "atol": 2e-2},
     }
+
+
+def dispatch_floor_us(torch, n=2000) -> float:
+    """Per-call time of back-to-back one-element fills on the current stream:
+    the launch-to-launch floor any kernel of this library pays."""
+    x = torch.zeros(1, device="cuda")
+    for _ in range(50):
+        x.fill_(1.0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        x.fill_(1.0)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1e3
+
+
+def device_info(torch) -> dict:
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "max_sclk_mhz": (props.clock_rate / 1000.0) if getattr(props, "clock_rate", 0) else None,
+            "sclk_now_mhz": None}
+    try:  # the current shader clock, from a child process (no GPU work of ours)
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        for card in json.loads(r.stdout).values():
+            for key, val in card.items():
+                if "sclk" in key.lower():
+                    info["sclk_now_mhz"] = float(str(val).strip("()Mhz "))
+    except Exception:
+        pass
+    return info
 
 
 def load_traffic(steps_kernel_ms):
@@ -316,7 +369,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", default="all",
                     help="comma list of extra workloads to measure besides the headline, or 'all'/'none'")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle legs (oracle timing and the per-workload error against it)")
     ap.add_argument("--no-cache-step", action="store_true",
                     help="skip the decode-step-over-a-cache timings (update + attention, fused)")
     ap.add_argument("--no-next-rows", action="store_true",
@@ -333,6 +387,13 @@ def main(argv=None) -> int:
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    # The oracle's worker processes start before anything touches the GPU.
+    pool = None
+    if not args.no_cpu_baseline:
+        from oracle.pool import OraclePool
+        pool = OraclePool()
+        log(f"oracle pool: {pool.workers} worker processes (host cores in the affinity mask)")
+
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -346,7 +407,10 @@ def main(argv=None) -> int:
     elif args.workloads != "none":
         names += [n for n in args.workloads.split(",") if n and n != HEADLINE]
 
-    results = {}
+    floor = dispatch_floor_us(torch)
+    log(f"dispatch floor (back-to-back one-element fills): {floor:.2f} us/call")
+
+    results, kept = {}, {}
     headline = None
     for name in names:
         w = synth.WORKLOADS[name]
@@ -366,17 +430,20 @@ def main(argv=None) -> int:
         rc, plan = _lib.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.d, int(w.causal), w.window,
                                   w.softcap, 0 if w.dtype == "bf16" else 1)
         sp = r.spread(ms)
+        same = determinism(r)
         results[name] = {"ms": ms, "steps": steps, "copies": copies, **fig,
-                         "kernel": kernel_name(plan, w), "spread": sp,
+                         "kernel": kernel_name(plan, w), "spread": sp, "memcmp_deterministic": same,
                          "plan": plan, "shape": w.describe()}
         log(f"{name}: {ms * 1e3:.2f} us/call  {fig['value']:.1f} {fig['unit']}  "
             f"({100 * fig['frac']:.1f}% of {fig['bound']} peak); rounds: median "
-            f"{sp['median_ms'] * 1e3:.2f} us, p10 {sp['p10_ms'] * 1e3:.2f}, p90 {sp['p90_ms'] * 1e3:.2f}")
+            f"{sp['median_ms'] * 1e3:.2f} us, p10 {sp['p10_ms'] * 1e3:.2f}, p90 {sp['p90_ms'] * 1e3:.2f}; "
+            f"same bytes over 3 calls: {same}")
         if name in CACHE_STEP_WORKLOADS and not args.no_cache_step:
             st = cache_step(r, steps, warmup)
             results[name]["cache_step"] = st
             log(f"{name} as a cache step: update + attention {st['update_then_attention_ms'] * 1e3:.2f} us, "
                 f"fused {st['fused_ms'] * 1e3:.2f} us")
+        kept[name] = (w, r.host, r.output_f64(0))
         if name == HEADLINE:
             headline = (r, ms, steps, fig)
         else:
@@ -417,9 +484,9 @@ def main(argv=None) -> int:
         log(f"copy calibration: 5 x {COPY_BYTES} bytes read + written")
         del src, dst
 
+    dev = device_info(torch)
     r, ms, steps, fig = headline
     w = r.w
-    gpu_out = r.output_f64((steps - 1) % len(r.outs))
     traffic = load_traffic(ms)
     line = {
         "metric": METRIC,
@@ -441,19 +508,41 @@ def main(argv=None) -> int:
                      "unit": "GB/s", "frac": fig["frac"], "traffic": traffic,
                      "kernel": results[HEADLINE]["kernel"],
                      "alg_bytes_per_launch": fig["alg_bytes"]},
-        "workloads": {n: {k: v for k, v in res.items() if k not in ("shape",)}
-                      for n, res in results.items()},
-        "next_rows": results_next,
-        "device": torch.cuda.get_device_name(0),
-        "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
-        "torch": torch.__version__,
-        "hip": torch.version.hip,
     }
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(r, gpu_out)
+    pre = "prefill_gqa8_L4096_w1024_cap50"
+    if pre in results:
+        rp = results[pre]
+        line["roofline_prefill"] = {"bound": "mfma", "achieved": rp["value"], "peak": MFMA_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": rp["frac"], "traffic": None,
+                                    "kernel": rp["kernel"], "alg_flops_per_launch": rp["alg_flops"],
+                                    "ms_per_launch": rp["ms"]}
+    if pool is not None:
+        log("oracle legs (every workload, whole input, process pool) ...")
+        for name, (wk, host, gpu_out) in kept.items():
+            leg = oracle_leg(pool, wk, host, gpu_out, runs=1 if wk.Lq * wk.Lkv >= (1 << 24) else 3)
+            results[name].update(leg)
+            log(f"{name}: oracle {leg['oracle']['seconds']:.3f} s on {pool.workers} processes; "
+                f"max abs err {leg['parity']['max_abs_err']:.3e}, allclose {leg['parity']['allclose']}")
+        pool.close()
+        o = results[HEADLINE]["oracle"]
+        line["cpu_baseline"] = {
+            "value": o["value"], "unit": o["unit"], "cores": o["cores"], "kind": "oracle",
+            "sample": f"whole {w.name} input ({w.B * w.Hq * w.Lq} query rows x {w.Lkv} keys), float64 oracle "
+                      f"head by head in a pool of {o['cores']} processes, median of {o['runs']} runs",
+            "seconds": o["seconds"], "blas": blas_config(),
+        }
     else:
         line["cpu_baseline"] = None
+    line.update({
+        "workloads": {n: {k: v for k, v in res.items() if k not in ("shape",)} for n, res in results.items()},
+        "next_rows": results_next,
+        "dispatch_floor_us": floor,
+        "device": dev,
+        "host_cores": len(os.sched_getaffinity(0)),
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+        "kernel_source_sha256": kernel_source_hash(),
+    })
     print(json.dumps(line), flush=True)
     return 0
 

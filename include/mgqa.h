@@ -165,7 +165,11 @@ int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const floa
  *         its rows; 128-row workgroups for head size 128, 256-row otherwise),
  *         1 = split-KV kernel (decode, multi-token decode and
  *         short sequences: the waves of a workgroup, and possibly several
- *         workgroups, split the key band of its rows)
+ *         workgroups, split the key band of its rows),
+ *         2 = short-band kernel (three 16-row blocks over a key band of at
+ *         most 768 keys, head size 49..96, e.g. the 729-token encoder: each
+ *         of 8 waves takes its own contiguous keys; info[4] is the most keys
+ *         one wave takes)
  * info[1] workgroups launched
  * info[2] query rows (head, position pairs) per workgroup
  * info[3] key splits per block of rows (1 on the prefill path); workgroups =

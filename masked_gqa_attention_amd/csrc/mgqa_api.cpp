@@ -70,6 +70,7 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   Plan p = {};
   const int G = Hq / Hkv;
   p.dqk = (d + 31) / 32;
+  p.qk_pad = 32 * p.dqk;
   p.dv = (d <= 80 && d > 64) ? 5 : 2 * p.dqk;  // 72 and 80 use a 80-wide P.V
   const long long units = (long long)B * Hkv;
   const long long rows_all = (long long)G * Lq;
@@ -165,14 +166,13 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
       ns = (max_tiles + tps - 1) / tps;
     }
   }
-  // Three 16-row blocks over an unsplit band of at least four 128-key tiles
-  // (head size <= 96; the 729-token encoder): 8 waves over 256-key tiles, so
-  // each SIMD runs two waves with half of the tiles each (encoder 15.0 ->
-  // 13.9 us).  The instance fits 256 registers only with the matrix-core
-  // accumulators in architectural registers (build flag).
-  if (p.nqb == 3 && ns == 1 && p.dv <= kSplitWideMaxDv && max_band_tiles(kSplitKeys) >= kSplitWide3MinTiles) {
-    p.nwaves = kSplitWavesWide;
-    p.keys_per_tile = 32 * kSplitWavesWide;
+  // Three 16-row blocks over an unsplit band of at most 768 keys, head size
+  // 49..96 (the 729-token encoder and shapes like it): the short-band kernel,
+  // eight waves that each take their own contiguous keys of the band.
+  if (p.nqb == kEncNqb && ns == 1 && d > 48 && d <= 96 && max_band_tiles(32) <= kEncMaxSteps) {
+    p.path = kPathShort;
+    p.nwaves = kEncWaves;
+    p.keys_per_tile = 32 * kEncSteps;  // the most keys one wave takes
   }
   p.nsplit = (int)ns;
   p.tiles_per_split = tps;
@@ -284,7 +284,7 @@ int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   info[2] = p.rows_per_wg;
   info[3] = p.nsplit;
   info[4] = p.keys_per_tile;
-  info[5] = p.dqk * 32;
+  info[5] = p.qk_pad;
   info[6] = p.dv * 16;
   info[7] = (long long)p.ws_bytes;
   info[8] = p.ncol > 0 ? p.ncol : 1;

@@ -19,16 +19,22 @@ constexpr int kPipe4Keys = 32;
 constexpr int kSplitWaves = 4;
 constexpr int kSplitKeys = 32 * kSplitWaves;
 // Wide split workgroups: 8 waves over 256-key tiles, for one 16-row block with
-// a long key range per workgroup (decode), or three 16-row blocks over a short
-// unsplit key band (encoder-sized sequences).
+// a long key range per workgroup (decode).
 constexpr int kSplitWavesWide = 8;
 constexpr int kSplitWideMinTiles = 8;  // 128-key tiles per workgroup from which they are used
-constexpr int kSplitWide3MinTiles = 4; // the same for three 16-row blocks (unsplit bands)
 constexpr int kSplitMaxNqb = 4;     // 16-row blocks per workgroup, head size <= 96
 constexpr int kSplitMaxNqbWide = 2; // head size > 96 (register budget)
 constexpr int kSplitWideMaxDv = 6;  // P.V 16-column blocks up to which 3 and 4 row blocks exist
 
-enum Path { kPathPrefill = 0, kPathSplit = 1 };
+// Short-band kernel (encoder-sized sequences): 8 waves x three 16-row
+// blocks per workgroup; each wave takes up to three 32-key steps of the
+// block's key band, so a band of at most 24 steps (768 keys) fits.
+constexpr int kEncWaves = 8;
+constexpr int kEncSteps = 3;
+constexpr int kEncNqb = 3;
+constexpr int kEncMaxSteps = kEncWaves * kEncSteps;
+
+enum Path { kPathPrefill = 0, kPathSplit = 1, kPathShort = 2 };
 
 // Division by a launch constant without a divide sequence: for 0 <= x < 2^31,
 // x / d == (x * m) >> (31 + s) with s = ceil(log2 d) and m = ceil(2^(31+s) / d)
@@ -83,6 +89,7 @@ struct KernelArgs {
 struct Plan {
   int path;
   int dqk;            // 32-wide head-size steps for Q.K^T
+  int qk_pad;         // head size Q.K^T is contracted over (padded)
   int dv;             // 16-wide head-size blocks for P.V
   int nqb;            // 16-row query blocks per wave
   int nwaves;         // waves per workgroup

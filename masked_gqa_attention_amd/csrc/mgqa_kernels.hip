@@ -89,6 +89,19 @@ struct Elem<_Float16> {
   }
 };
 
+// All-ones matrix-core operand (two 16-bit 1.0 per dword): multiplying it by
+// P^T gives the row sums of P in every row of the result.
+template <typename T>
+struct OnesOperand;
+template <>
+struct OnesOperand<__bf16> {
+  static constexpr uint32_t kPair = 0x3F803F80u;  // two bf16 1.0
+};
+template <>
+struct OnesOperand<_Float16> {
+  static constexpr uint32_t kPair = 0x3C003C00u;  // two fp16 1.0
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
@@ -389,7 +402,7 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
 template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SOFTCAP, bool MASK>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, int kbase, int kglob0,
                                           const u32x4 (&qf)[NQB][DQK], const int (&qpos)[NQB],
-                                          float (&m_e)[NQB], float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                          float (&m_e)[NQB], f32x4 (&ls)[NQB], f32x4 (&o)[NQB][DV],
                                           const KernelArgs& a, int c16, int g4, bool rmask = true) {
   // ---- S^T = K Q^T -------------------------------------------------------
   f32x4 s[NQB][2];
@@ -446,7 +459,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
       const bool up = mxe[qb] > m_e[qb] + kRescaleSlack;
       const float f = up ? fast_exp2(m_e[qb] - mxe[qb]) : 1.0f;  // 0 when m_e was -inf
       if (up) m_e[qb] = mxe[qb];
-      l_p[qb] *= f;
+      ls[qb] *= f;
 #pragma unroll
       for (int db = 0; db < DV; ++db) o[qb][db] *= f;
     }
@@ -473,9 +486,17 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
         }
         p[hh * 4 + i] = pv;
       }
-    l_p[qb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     pk[qb] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]),
                    Elem<T>::pack2(p[4], p[5]), Elem<T>::pack2(p[6], p[7])};
+  }
+  // Row sums on the matrix cores from the same 16-bit probabilities that
+  // enter P.V (an all-ones A operand): every lane of column c16 receives the
+  // sum over the step's 32 keys, so a constant V comes back exactly.
+  {
+    const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
+                        OnesOperand<T>::kPair};
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) ls[qb] = Elem<T>::mfma(ones, pk[qb], ls[qb]);
   }
 
   // ---- O^T += V^T P^T ---------------------------------------------------------
@@ -495,14 +516,14 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
 template <typename T, int DQK, int DV, int NQB, int KP, int VP, bool SOFTCAP>
 __device__ __forceinline__ void tile_pair(const uint16_t* Ks, const uint16_t* Vs, int k0, bool full,
                                           const u32x4 (&qf)[NQB][DQK], const int (&qpos)[NQB],
-                                          float (&m_e)[NQB], float (&l_p)[NQB], f32x4 (&o)[NQB][DV],
+                                          float (&m_e)[NQB], f32x4 (&ls)[NQB], f32x4 (&o)[NQB][DV],
                                           const KernelArgs& a, int c16, int g4) {
 #pragma unroll
   for (int kb = 0; kb < 64; kb += 32) {
     if (full)
-      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, kb, k0, qf, qpos, m_e, ls, o, a, c16, g4);
     else
-      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, kb, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, kb, k0, qf, qpos, m_e, ls, o, a, c16, g4);
   }
 }
 
@@ -571,12 +592,12 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   }
   const int t_begin = key_lo / KEYS, t_end = key_hi / KEYS + 1;
 
-  float m_e[NQB], l_p[NQB];
-  f32x4 o[NQB][DV];
+  float m_e[NQB];
+  f32x4 ls[NQB], o[NQB][DV];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m_e[qb] = kNegInf;
-    l_p[qb] = 0.f;
+    ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -607,7 +628,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
     }
     // Two 32-key steps per tile; K fragments of the second step are read
     // during the first step's products.
-    tile_pair<T, DQK, DV, NQB, KP, VP, SOFTCAP>(Ks, Vs, k0, full, qf, qpos, m_e, l_p, o, a, c16, g4);
+    tile_pair<T, DQK, DV, NQB, KP, VP, SOFTCAP>(Ks, Vs, k0, full, qf, qpos, m_e, ls, o, a, c16, g4);
     if (t + 1 < t_end) {
       uint16_t* nxt = smem + (cur ^ 1) * STAGE;
       kt.store(nxt, tid);
@@ -617,10 +638,8 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   }
 
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float l = col_sum(l_p[qb]);
-    if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / l, d, g4);
-  }
+  for (int qb = 0; qb < NQB; ++qb)
+    if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / ls[qb][0], d, g4);
 }
 
 // ---------------------------------------------------------------------------
@@ -636,10 +655,13 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 // the same 16-bit probabilities that enter P.V.
 //
 // Fixed reference (FIXREF): with a softcap c, every score lies in [-c, c], so
-// exp2 of a softcapped score (base-2 units) minus c*log2(e) - 40 lies in
-// [2^(40 - 2c log2 e), 2^40].  For c <= 57.5 that is inside the normal range
-// of fp32 and bf16: no running maximum and no rescale are needed.  Otherwise
-// the running maximum is kept with the lazy rescale.
+// exp2 of a softcapped score (base-2 units) minus c*log2(e) - 64 lies in
+// [2^(64 - 2c log2 e), 2^64].  For c <= 57.5 (c*log2(e) <= 83) the smallest
+// probability is at least 2^-102: its products with values down to 2^-24
+// inside P.V stay in the normal range of fp32, and the largest, 2^64, leaves
+// room for sums over 2^23 keys and values up to 2^40.  No running maximum and
+// no rescale are needed.  Otherwise the running maximum is kept with the lazy
+// rescale.
 //
 // Workgroup: four waves (one per SIMD), 128 rows, one 32-key tile per step.
 // LDS holds five stages of one K and one V tile (16 KB per stage pair), all
@@ -655,16 +677,6 @@ constexpr int kPipe4Stages = 5;
 constexpr int kPipe4Tile = 32 * 128;                       // elements of one K or V tile
 constexpr int kPipe4VRegion = kPipe4Stages * kPipe4Tile;  // first V tile (elements)
 
-template <typename T>
-struct OnesOperand;
-template <>
-struct OnesOperand<__bf16> {
-  static constexpr uint32_t kPair = 0x3F803F80u;  // two bf16 1.0
-};
-template <>
-struct OnesOperand<_Float16> {
-  static constexpr uint32_t kPair = 0x3C003C00u;  // two fp16 1.0
-};
 
 // Per-lane fragment offsets (elements): ka[t] -> K row c16, chunk 4t+g4 of
 // tile row 0 (swizzled slot); va[db] -> the transposed V read of columns
@@ -717,7 +729,7 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
                       OnesOperand<T>::kPair};
   float mref[2], resc[2] = {1.0f, 1.0f};
   if constexpr (FIXREF) {
-    mref[0] = mref[1] = a.c2 - 40.0f;
+    mref[0] = mref[1] = a.c2 - 64.0f;
   } else {
     if (mask) {
 #pragma unroll
@@ -1229,12 +1241,12 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     load_q<DQK>(qf[qb], qg + roff, rok, d, g4);
   }
 
-  float m_e[NQB], l_p[NQB];
-  f32x4 o[NQB][DV];
+  float m_e[NQB];
+  f32x4 ls[NQB], o[NQB][DV];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m_e[qb] = kNegInf;
-    l_p[qb] = 0.f;
+    ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -1255,12 +1267,12 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     // different registers on the two paths, merged by register moves on
     // every tile.
     if constexpr (NQB > 1)
-      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4,
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, ls, o, a, c16, g4,
                                                         !full);
     else if (full)
-      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, ls, o, a, c16, g4);
     else
-      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16, g4);
+      tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, ls, o, a, c16, g4);
   };
   if constexpr (TWO_AHEAD) {
     // Tiles alternate between the two register sets; each set is refilled
@@ -1305,13 +1317,13 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
         if (!a.causal) full = full && (w0 + 31 - pos_min < a.window);
       }
       if constexpr (NQB > 1)  // one copy of the step, as in compute() above
-        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
+        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, ls, o, a, c16,
                                                           g4, !full);
       else if (full)
-        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
+        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, false>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, ls, o, a, c16,
                                                            g4);
       else
-        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, l_p, o, a, c16,
+        tile_step<T, DQK, DV, NQB, KP, VP, SOFTCAP, true>(Ks, Vs, 32 * wave, k0, qf, qpos, m_e, ls, o, a, c16,
                                                           g4);
     }
   }
@@ -1336,10 +1348,9 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   __syncthreads();  // the tiles are no longer read
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const float l = col_sum(l_p[qb]);
     if (g4 == 0) {
       wm[wave][16 * qb + c16] = m_e[qb];
-      wl[wave][16 * qb + c16] = l;
+      wl[wave][16 * qb + c16] = ls[qb][0];
     }
 #pragma unroll
     for (int db = 0; db < DV; ++db)
@@ -1456,6 +1467,298 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     __hip_atomic_store(a.ws_cnt + grp * NCOL + half, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Short-band kernel (encoder-sized sequences).
+//
+// One workgroup of 8 waves per (unit, block of 48 rows).  The block's key
+// band, at most 768 keys, is cut into 8 contiguous wave ranges of up to three
+// 32-key steps.  A wave reads only its own keys: its K fragments go straight
+// from memory into registers (the A operand of S^T = K Q^T takes 8
+// consecutive head-size elements of one key per lane: a piece of a row-major
+// K row), and its V rows go into a private LDS region through direct
+// global-to-LDS loads, from where the transposing LDS read builds V^T.  No
+// tile is shared between waves, so the key loop has no barrier.
+//
+// With every score of its range in registers, a wave takes the row maximum
+// once and one exponential per score (two passes over registers): no running
+// maximum and no rescale.  Row sums come from the matrix cores (all-ones A
+// operand, the same 16-bit P as P.V).  The eight wave states then merge in
+// LDS in wave order; once a wave's P.V products are done, its region holds
+// its unnormalised rows (48 rows x DV*16 floats, exactly the region's bytes).
+//
+// Q.K^T contracts the head size in DQK 32-deep matrix-core steps (head size
+// 72 padded to 96 with zeros).  A 16-deep product chained onto 32-deep ones
+// through the accumulator was tried for 72 -> 80 and gave wrong results with
+// this compiler (the chained product read an accumulator that was not yet
+// written); every accumulator chain here uses one product shape.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV, bool SOFTCAP>
+__global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
+  constexpr int NW = kEncWaves, NS = kEncSteps, NQB = kEncNqb;
+  constexpr int VPITCH = DV * 16;           // elements of one staged V row
+  constexpr int CPR = DV * 2;               // 16-byte chunks of one staged V row
+  constexpr int VLOADS = 32 * CPR / 64;     // 64-lane direct-to-LDS loads per step
+  constexpr int REGION = NS * 32 * VPITCH;  // elements of one wave's V region
+  constexpr int OPITCH = DV * 16;           // floats of one output row in the merge
+  static_assert(DQK >= 1, "at least one 32-deep step");
+  static_assert((32 * CPR) % 64 == 0, "a step's V rows are whole 64-lane loads");
+  static_assert(NQB * 16 * OPITCH * 4 == REGION * 2, "a wave's output rows fill its V region exactly");
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NW * REGION];
+  __shared__ float wm[NW][NQB * 16], wl[NW][NQB * 16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int g4 = lane >> 4, c16 = lane & 15;
+  // Every argument the first loads depend on, asked for at once.
+  const long long kv_stride = a.kv_stride;
+  asm volatile("" : : "s"(kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
+               "s"(a.G), "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.d), "s"(a.causal), "s"(a.window), "s"(a.div_g.m),
+               "s"(a.div_g.s), "s"(a.div_npos.m), "s"(a.div_npos.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s),
+               "s"(a.nwg));
+  // XCD-contiguous numbering, as in the other kernels: the position blocks
+  // of one unit share its K/V rows in one L2.
+  int lin = blockIdx.x;
+  if ((a.nwg & 7) == 0) lin = (lin & 7) * (a.nwg >> 3) + (lin >> 3);
+  const int unit = fdiv(lin, a.div_npos);
+  const int pblk = lin - unit * a.n_pos_blk;
+  const int b = fdiv(unit, a.div_hkv), kvh = unit - b * a.Hkv;
+  const int G = a.G, d = a.d;
+  const int off = a.Lkv - a.Lq;
+  const int q0 = pblk * a.m;
+  const int m_eff = min(a.m, a.Lq - q0);
+  const int nrows = m_eff * G;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)unit * kv_stride;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)unit * kv_stride;
+  uint16_t* og = static_cast<uint16_t*>(a.out);
+
+  // Key band of the block, and this wave's share of its 32-key steps.
+  const int pos_min = q0 + off, pos_max = q0 + m_eff - 1 + off;
+  int key_lo = 0, key_hi = a.Lkv - 1;
+  if (a.causal) key_hi = min(key_hi, pos_max);
+  if (a.window > 0) {
+    key_lo = max(0, pos_min - a.window + 1);
+    if (!a.causal) key_hi = min(key_hi, pos_max + a.window - 1);
+  }
+  const int kb0 = key_lo & ~31;
+  const int nsteps = (key_hi - kb0) / 32 + 1;  // at most NW * NS (the plan checks)
+  const int spw = (nsteps + NW - 1) / NW;
+  const int my = max(0, min(spw, nsteps - wave * spw));  // this wave's steps (wave-uniform)
+  const int kw0 = kb0 + 32 * wave * spw;                  // this wave's first key
+
+  // Keys at or past Lkv lie outside the descriptors' ranges and read as zero.
+  const uint32_t unit_bytes = (uint32_t)a.Lkv * (uint32_t)d * 2u;
+  const auto rs_k = make_rsrc(kg, unit_bytes);
+  const auto rs_v = make_rsrc(vg, unit_bytes);
+
+  // Q^T operands: lane column c16 is the row, lane group g4 holds head-size
+  // elements 32t + 8g4 .. +7 of step t.
+  u32x4 qf[NQB][DQK];
+  int qpos[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int r = 16 * qb + c16;
+    const bool rok = r < nrows;
+    const int pl = fdiv(r, a.div_g), hr = r - pl * G;
+    qpos[qb] = q0 + pl + off;
+    const uint16_t* qrow = qg + (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (rok ? q0 + pl : 0)) * d;
+#pragma unroll
+    for (int t = 0; t < DQK; ++t) {
+      const int col = 32 * t + 8 * g4;
+      qf[qb][t] = (rok && col < d) ? ldg16(qrow + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // K fragments of this wave's steps (registers) and its V rows (LDS), in
+  // step order so that the first step's scores wait for the least.
+  u32x4 kf[NS][2][DQK];
+  uint16_t* const myv = sv + wave * REGION;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (st < my) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t krow = (uint32_t)(kw0 + 32 * st + 16 * hh + c16) * (uint32_t)d * 2u;
+#pragma unroll
+        for (int t = 0; t < DQK; ++t) {
+          const int col = 32 * t + 8 * g4;
+          const uint32_t vo = col < d ? krow + (uint32_t)col * 2u : kOutOfRange;
+          kf[st][hh][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)vo, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const int n = 64 * i + lane;  // chunk n of the step's rows: row n / CPR, chunk n % CPR
+        const int row = n / CPR, ch = n - row * CPR;
+        const uint32_t vo =
+            ch * 8 < d ? ((uint32_t)(kw0 + 32 * st + row) * (uint32_t)d + (uint32_t)(ch * 8)) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs_v, (__attribute__((address_space(3))) void*)(myv + st * 32 * VPITCH + i * 512), 16, (int)vo, 0, 0,
+            0);
+      }
+    }
+  }
+
+  // ---- scores S^T = K Q^T of every step of the range -----------------------
+  f32x4 s[NS][2][NQB];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (st < my) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < DQK; ++t) acc = Elem<T>::mfma(kf[st][hh][t], qf[qb][t], acc);
+          s[st][hh][qb] = acc;
+        }
+    }
+  }
+
+  // ---- mask (steps crossing a band edge or the end of the keys) ------------
+  bool part[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int k0 = kw0 + 32 * st;
+    bool full = k0 + 32 <= a.Lkv;
+    if (a.causal) full = full && (k0 + 31 <= pos_min);
+    if (a.window > 0) {
+      full = full && (pos_max - k0 < a.window);
+      if (!a.causal) full = full && (k0 + 31 - pos_min < a.window);
+    }
+    part[st] = st < my && !full;
+    if (part[st]) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!key_visible(k0 + 16 * hh + 4 * g4 + i, qpos[qb], a.Lkv, a.causal, a.window))
+              s[st][hh][qb][i] = kNegInf;
+    }
+  }
+
+  // ---- row maxima over the whole range, then the probabilities --------------
+  // The softcap is increasing, so the maximum of the capped scores is the
+  // capped maximum score (same formula, so the maximum maps to exactly 2^0).
+  float m_e[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      if (st < my)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][hh][qb][i]);
+    mx = col_max(mx);
+    if (SOFTCAP)
+      m_e[qb] = (mx == kNegInf) ? kNegInf
+                                : __builtin_fmaf(fast_rcp(fast_exp2(mx * a.gamma) + 1.0f), -2.0f * a.c2, a.c2);
+    else
+      m_e[qb] = mx * a.alpha;
+  }
+  const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair};
+  u32x4 pk[NS][NQB];
+  f32x4 ls[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (st < my) {
+        float p[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = s[st][hh][qb][i];
+            float pv;
+            if (SOFTCAP) {
+              // c*tanh(u) = c - 2c/(exp(2u)+1), in base-2 exponent units.
+              const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
+              pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
+              if (part[st] && x == kNegInf) pv = 0.f;
+            } else {
+              pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
+            }
+            p[hh * 4 + i] = pv;
+          }
+        pk[st][qb] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]), Elem<T>::pack2(p[4], p[5]),
+                           Elem<T>::pack2(p[6], p[7])};
+        ls[qb] = Elem<T>::mfma(ones, pk[st][qb], ls[qb]);
+      }
+    }
+  }
+
+  // ---- O^T = V^T P^T over the range ------------------------------------------
+  // Transposed reads as in the other kernels: lane s of a 16-lane group points
+  // at key row 4*g4 + s/4 (and +16), columns 16*db + 4*(s%4).
+  f32x4 o[NQB][DV];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (st < my) {
+      const uint16_t* v0 = myv + (32 * st + 4 * g4 + (c16 >> 2)) * VPITCH + 4 * (c16 & 3);
+#pragma unroll
+      for (int db = 0; db < DV; ++db) {
+        const u32x2 lo = lds_read_tr4(v0 + 16 * db);
+        const u32x2 hi = lds_read_tr4(v0 + 16 * VPITCH + 16 * db);
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[st][qb], o[qb][db]);
+      }
+    }
+  }
+
+  // ---- merge the eight wave states in wave order -----------------------------
+  // The products above consumed this wave's V reads, so its region is free.
+  float* wo = reinterpret_cast<float*>(myv);
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (g4 == 0) {
+      wm[wave][16 * qb + c16] = m_e[qb];
+      wl[wave][16 * qb + c16] = ls[qb][0];
+    }
+#pragma unroll
+    for (int db = 0; db < DV; ++db)
+      *reinterpret_cast<f32x4*>(&wo[(16 * qb + c16) * OPITCH + 16 * db + 4 * g4]) = o[qb][db];
+  }
+  __syncthreads();
+  constexpr int C4 = DV * 4;  // float4 chunks of one output row
+  constexpr int JN = (NQB * 16 * C4 + 64 * NW - 1) / (64 * NW);
+#pragma unroll
+  for (int j = 0; j < JN; ++j) {
+    const int q = tid + j * 64 * NW;
+    const int r = q / C4, c4 = q - r * C4;
+    if (q >= NQB * 16 * C4 || r >= nrows || 4 * c4 >= d) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][r]);
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = wm[w][r] == kNegInf ? 0.f : fast_exp2(wm[w][r] - M);
+      L += f * wl[w][r];
+      acc += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(sv + w * REGION) + r * OPITCH + 4 * c4);
+    }
+    const float inv = 1.0f / L;
+    const int pr = fdiv(r, a.div_g);
+    const size_t oo = (((size_t)b * a.Hq + kvh * G + (r - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
+    *reinterpret_cast<u32x2*>(og + oo) =
+        u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
+  }
+}
+
 __global__ void zero_kernel(uint32_t* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -1478,20 +1781,11 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
   const dim3 grid((unsigned)plan.workgroups);
   if (plan.path == kPathSplit) {
     if (plan.nwaves == kSplitWavesWide) {
-      // Eight waves over 256-key tiles, full width: one 16-row block (long
-      // decode ranges), or three (short unsplit sequences, head size <= 96).
-      if (plan.ncol != 1) return hipErrorInvalidValue;
-      if (plan.nqb == 1) {
-        launch_split<T, DQK, DV, 1, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
-        return hipGetLastError();
-      }
-      if constexpr (DV <= kSplitWideMaxDv) {
-        if (plan.nqb == 3) {
-          launch_split<T, DQK, DV, 3, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
-          return hipGetLastError();
-        }
-      }
-      return hipErrorInvalidValue;
+      // Eight waves over 256-key tiles, full width, one 16-row block (long
+      // decode ranges).
+      if (plan.ncol != 1 || plan.nqb != 1) return hipErrorInvalidValue;
+      launch_split<T, DQK, DV, 1, SOFTCAP, 1, kSplitWavesWide>(grid, args, st);
+      return hipGetLastError();
     }
     if (plan.ncol == 2) {
       // Two column halves: each workgroup computes half of P.V's 16-column blocks.
@@ -1531,7 +1825,22 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
 }
 
 template <typename T, bool SOFTCAP>
+static hipError_t launch_short(const Plan& plan, const KernelArgs& args, hipStream_t st) {
+  const dim3 grid((unsigned)plan.workgroups), block(64 * kEncWaves);
+  if (args.d > 80 && args.d <= 96)
+    hipLaunchKernelGGL((encoder_kernel<T, 3, 6, SOFTCAP>), grid, block, 0, st, args);
+  else if (args.d > 64)
+    hipLaunchKernelGGL((encoder_kernel<T, 3, 5, SOFTCAP>), grid, block, 0, st, args);
+  else if (args.d > 48)
+    hipLaunchKernelGGL((encoder_kernel<T, 2, 4, SOFTCAP>), grid, block, 0, st, args);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T, bool SOFTCAP>
 static hipError_t launch_dims(const Plan& plan, const KernelArgs& args, hipStream_t st) {
+  if (plan.path == kPathShort) return launch_short<T, SOFTCAP>(plan, args, st);
   switch (plan.dqk * 16 + plan.dv) {
     case 1 * 16 + 2: return launch_typed<T, 1, 2, SOFTCAP>(plan, args, st);
     case 2 * 16 + 4: return launch_typed<T, 2, 4, SOFTCAP>(plan, args, st);

@@ -188,6 +188,7 @@ def test_plans_for_workloads():
     assert paths["decode_gqa4_kv8192"]["nsplit"] > 1
     assert paths["decode_gqa16_kv32768_w4096_cap30"]["path"] == 1
     assert paths["prefill_gqa8_L4096_w1024_cap50"]["path"] == 0
+    assert paths["encoder_siglip_L729_d72"]["path"] == 2
     assert paths["encoder_siglip_L729_d72"]["d_pv_pad"] == 80
     assert paths["encoder_siglip_L729_d72"]["d_qk_pad"] == 96
     # The decode band of the windowed decode covers only the last 4096 keys:
@@ -226,7 +227,7 @@ def test_encoder_shapes_split_keys_when_row_blocks_are_few():
     16 heads the row blocks already fill the chip and there is no split."""
     for H, want_split in ((1, True), (2, True), (4, True), (16, False)):
         rc, info = _lib.attn_plan(1, H, H, 729, 729, 72, 0, 0, 0.0)
-        assert rc == 0 and info["path"] == 1, info
+        assert rc == 0 and info["path"] == (1 if want_split else 2), info
         assert (info["nsplit"] > 1) == want_split, (H, info)
         assert info["workgroups"] >= 256 or info["nsplit"] > 1, (H, info)
 
@@ -249,10 +250,10 @@ def test_column_halves_plan():
 
 
 def test_wide_split_plan():
-    """A single 16-row block with at least eight 128-key tiles per workgroup,
-    or three 16-row blocks over an unsplit band of at least four, run 8 waves
-    over 256-key tiles; few tiles per workgroup, two or four row blocks or
-    column halves keep 4 waves over 128-key tiles."""
+    """A single 16-row block with at least eight 128-key tiles per workgroup
+    runs 8 waves over 256-key tiles; few tiles per workgroup, two, three or
+    four row blocks or column halves keep 4 waves over 128-key tiles (three
+    row blocks over short bands take the short-band kernel)."""
     rc, info = _lib.attn_plan(8, 32, 8, 1, 8192, 128, 1, 0, 0.0)     # 4 splits of 16 tiles
     assert rc == 0 and info["keys_per_tile"] == 256 and info["ncol"] == 1, info
     rc, info = _lib.attn_plan(64, 64, 8, 1, 3000, 72, 1, 0, 0.0)     # no split, 24 tiles
@@ -261,11 +262,35 @@ def test_wide_split_plan():
     assert rc == 0 and info["keys_per_tile"] == 128 and info["ncol"] == 2, info
     rc, info = _lib.attn_plan(1, 4, 1, 64, 64, 128, 1, 0, 0.0)         # one tile
     assert rc == 0 and info["keys_per_tile"] == 128, info
-    rc, info = _lib.attn_plan(1, 16, 16, 729, 729, 72, 0, 0, 0.0)      # 48-row blocks, 6 tiles
-    assert rc == 0 and info["keys_per_tile"] == 256 and info["rows_per_wg"] == 48, info
-    rc, info = _lib.attn_plan(5, 16, 16, 190, 190, 72, 0, 0, 0.0)      # 48-row blocks, 2 tiles
-    assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 48, info
+    rc, info = _lib.attn_plan(1, 16, 16, 729, 1500, 72, 1, 0, 0.0)     # 48-row blocks, long band
+    assert rc == 0 and info["path"] == 1 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 48, info
     rc, info = _lib.attn_plan(1, 16, 16, 700, 900, 80, 1, 300, 0.0)    # 32-row blocks
     assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 32, info
     rc, info = _lib.attn_plan(1, 48, 16, 729, 729, 40, 1, 0, 0.0)      # 64-row blocks
     assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 64, info
+
+
+def test_short_band_plan():
+    """Three 16-row blocks over an unsplit band of at most 768 keys and head
+    sizes 49..96 take the short-band kernel (path 2, no workspace, 96 keys per
+    wave at most); longer bands, head size 48 or 128, and shapes with key
+    splits do not."""
+    def plan(*a):
+        rc, info = _lib.attn_plan(*a)
+        assert rc == 0, a
+        return info
+    for d in (56, 64, 72, 80, 88, 96):
+        info = plan(1, 16, 16, 729, 729, d, 0, 0, 0.0)
+        assert info["path"] == 2 and info["rows_per_wg"] == 48 and info["keys_per_tile"] == 96, (d, info)
+        assert info["workspace_bytes"] == 0 and info["nsplit"] == 1 and info["workgroups"] == 256, (d, info)
+        assert info["d_qk_pad"] == 32 * ((d + 31) // 32), (d, info)
+    assert plan(1, 16, 16, 729, 729, 48, 0, 0, 0.0)["path"] == 1
+    assert plan(1, 16, 16, 729, 729, 128, 0, 0, 0.0)["path"] == 1
+    assert plan(1, 16, 16, 729, 768, 72, 1, 0, 0.0)["path"] == 2     # band of exactly 768 keys
+    assert plan(1, 16, 16, 729, 769, 72, 1, 0, 0.0)["path"] == 1     # 769 keys: 25 steps
+    assert plan(1, 4, 4, 729, 729, 72, 0, 0, 0.0)["path"] == 1       # few heads: key splits
+    assert plan(1, 16, 8, 800, 800, 80, 1, 300, 30.0)["path"] == 2   # two heads per kv head
+    # ring buffers need the decode path
+    P = ctypes.c_void_p(0x100000)
+    rc = _lib.attn_fwd_cache(P, P, P, P, 1, 16, 16, 729, 729, 729, 5, 72, 0, 0, 0.0, 0, None, 0, None)
+    assert rc == _lib.MGQA_ERR_UNSUPPORTED

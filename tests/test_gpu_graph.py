@@ -93,3 +93,43 @@ def test_fused_cache_step_in_a_graph():
         call(out)
     _replays(g, out, want)
     assert torch.equal(kc.view(torch.int16), k_after.view(torch.int16))
+
+
+def test_api_attn_two_graphs_replayed_in_reverse_order():
+    """Two graphs of one split-decode shape captured through api.attn, each
+    with its own workspace (zero-filled before capture), replayed in the
+    reverse order of capture with eager work in between: every replay equals
+    the eager call bit for bit.  Capturing a call whose plan needs a workspace
+    without passing one raises instead of sharing the eager cache."""
+    from masked_gqa_attention_amd import api
+    announce("graph two captures through api.attn")
+    B, Hq, Hkv, Lq, Lkv, d = 2, 8, 2, 1, 3000, 128
+    q1 = to_device(synth.draw_array(620, (B, Hq, Lq, d)), "bf16")
+    q2 = to_device(synth.draw_array(621, (B, Hq, Lq, d)), "bf16")
+    k = to_device(synth.draw_array(622, (B, Hkv, Lkv, d)), "bf16")
+    v = to_device(synth.draw_array(623, (B, Hkv, Lkv, d)), "bf16")
+    want1 = api.attn(q1, k, v, causal=True)
+    want2 = api.attn(q2, k, v, causal=True)
+    ws1 = api.workspace_for(q1, Hkv, Lkv, causal=True)
+    ws2 = api.workspace_for(q2, Hkv, Lkv, causal=True)
+    assert ws1 is not None and ws2 is not None
+    out1, out2 = torch.empty_like(q1), torch.empty_like(q2)
+    torch.cuda.synchronize()
+    g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        api.attn(q1, k, v, causal=True, out=out1, workspace=ws1)
+    with torch.cuda.graph(g2):
+        api.attn(q2, k, v, causal=True, out=out2, workspace=ws2)
+    for r in range(3):
+        for g, out, want in ((g2, out2, want2), (g1, out1, want1)):
+            torch.ones(1024, device="cuda").mul_(2.0)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {r} differs"
+    x = torch.ones(16, device="cuda")
+    g3 = torch.cuda.CUDAGraph()
+    with pytest.raises(ValueError, match="workspace"):
+        with torch.cuda.graph(g3):
+            x.mul_(2.0)
+            api.attn(q1, k, v, causal=True)
+    torch.cuda.synchronize()

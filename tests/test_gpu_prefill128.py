@@ -10,9 +10,15 @@ against the float64 oracle, on shapes chosen to reach each of its paths:
   ragged lengths that are not multiples of the 32-key tile, bottom-right
   causal alignment with Lq < Lkv, a non-causal (two-sided) window.
 
-Every case asserts that the plan takes the prefill path with head size 128,
-and compares sampled rows (all band edges plus seeded random rows) element
-by element; the smaller ones are compared in full.
+Every case asserts that the plan takes the prefill path with head size 128
+and compares every output element with the float64 oracle (run head by head
+in a process pool for the larger shapes).
+
+The anti-aligned batches ("fixref_cap50_hot", "fixref_cap57p5_floor") push
+every visible score to the softcap's lower bound -c.  At c = 57.5, the largest
+softcap that keeps the fixed reference, the smallest probability is about
+2^-126, so its products with values below 1 sit below the float32 normal
+range inside the P.V products; the case shows the output still matches.
 """
 import numpy as np
 import pytest
@@ -33,6 +39,8 @@ from .gpu_util import announce, run  # noqa: E402
 # name, B, Hq, Hkv, Lq, Lkv, causal, window, softcap, dtype, q scale, seed
 CASES = [
     ("fixref_cap50_hot", 2, 16, 2, 1024, 1024, True, 300, 50.0, "bf16", 12.0, 301),
+    ("fixref_cap57p5_floor", 2, 16, 2, 1024, 1024, True, 300, 57.5, "bf16", 12.0, 311),
+    ("fixref_cap57p5_floor_short_rows", 2, 64, 8, 300, 300, True, 0, 57.5, "bf16", 12.0, 312),
     ("fixref_cap57_ragged", 2, 32, 4, 777, 1061, True, 0, 57.0, "bf16", 8.0, 302),
     ("runmax_cap58", 2, 32, 4, 777, 1061, True, 0, 58.0, "bf16", 8.0, 303),
     ("runmax_cap500_window", 2, 16, 2, 1040, 1040, True, 129, 500.0, "bf16", 30.0, 304),
@@ -45,29 +53,12 @@ CASES = [
 ]
 
 
-def _rows(B, Hq, Lq, Lkv, window, seed, n_random=160):
-    rng = np.random.default_rng(seed)
-    off = Lkv - Lq
-    edges = {0, 1, 31, 32, 33, 63, 64, Lq // 2, Lq - 33, Lq - 32, Lq - 2, Lq - 1}
-    if window > 0:
-        for w in (window - 1, window, window + 1):
-            edges.update({w - off - 1, w - off, w - off + 1, w - 1, w})
-    rows = set()
-    for i in edges:
-        if 0 <= i < Lq:
-            for b in range(B):
-                rows.update({(b, 0, i), (b, Hq - 1, i), (b, int(rng.integers(Hq)), i)})
-    while len(rows) < 3 * B * len(edges) + n_random:
-        rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Lq))))
-    return sorted(rows)
-
-
 def _inputs(name, B, Hq, Hkv, Lq, Lkv, dtype, qscale, seed):
     q = synth.draw_array(seed, (B, Hq, Lq, 128), dtype)
     k = synth.draw_array(seed + 1, (B, Hkv, Lkv, 128), dtype)
     v = synth.draw_array(seed + 2, (B, Hkv, Lkv, 128), dtype)
     qf = synth.storage_to_f64(q, dtype) * qscale
-    if name.startswith("fixref_cap50"):
+    if "_floor" in name or name.startswith("fixref_cap50"):
         # Batch 1: every query anti-aligned with every key, so each visible
         # score is pushed to the softcap's lower bound.
         kf = synth.storage_to_f64(k, dtype)
@@ -82,7 +73,7 @@ def _inputs(name, B, Hq, Hkv, Lq, Lkv, dtype, qscale, seed):
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
-def test_prefill128_parity(case):
+def test_prefill128_parity(case, oracle_pool):
     from masked_gqa_attention_amd import _lib
     name, B, Hq, Hkv, Lq, Lkv, causal, window, softcap, dtype, qscale, seed = case
     rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, 128, int(causal), window, softcap,
@@ -93,17 +84,12 @@ def test_prefill128_parity(case):
     got = run(q, k, v, dtype, causal, window, softcap)
     assert np.isfinite(got).all()
     qf, kf, vf = (synth.storage_to_f64(a, dtype) for a in (q, k, v))
-    if B * Hq * Lq * Lkv <= 24 * 1024 * 1024:
-        ref = oracle.attention(qf, kf, vf, causal, window, softcap)
-        ok, st = compare(got, ref)
-    else:
-        rows = _rows(B, Hq, Lq, Lkv, window, seed)
-        ref = oracle.attention_rows(qf, kf, vf, rows, causal, window, softcap)
-        ok, st = compare(np.stack([got[b, h, i] for (b, h, i) in rows]), ref)
-    print(name, st, flush=True)
+    ref = oracle_pool.attention(qf, kf, vf, causal, window, softcap)
+    ok, st = compare(got, ref)
+    print(name, st, f"{got.size} elements compared", flush=True)
     assert ok, f"{name}: {st}"
     assert st["nrmse"] < 1e-2, f"{name}: {st}"
-    if name.startswith("fixref_cap50"):
+    if "_floor" in name or name.startswith("fixref_cap50"):
         # The constructed batch really sits at the lower bound: its scaled
         # scores are all below -c/2 before the softcap.
         G = Hq // Hkv

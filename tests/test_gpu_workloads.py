@@ -1,10 +1,8 @@
 """Parity at the full sizes of the five named workloads, in the launch
-configuration the benchmark times (the same attn_fwd_ex call, same plan).
-The float64 oracle checks every output element where it finishes in seconds
-(the decode and encoder workloads and the tiny one); for the 4096-token
-prefill it checks sampled rows one by one, chosen to include every band
-edge (first rows, rows around the window length, last rows) plus seeded
-random rows across batches and heads."""
+configuration the benchmark times (the same attn_fwd_ex call, same plan),
+and of large prefill-path shapes.  The float64 oracle checks every output
+element; the large shapes run it head by head in a process pool (the
+oracle_pool fixture) so the 4096-token prefill finishes in seconds."""
 import numpy as np
 import pytest
 
@@ -22,24 +20,8 @@ if not torch.cuda.is_available():  # pragma: no cover
 from .gpu_util import announce, run  # noqa: E402
 
 
-def _sample_rows(w, n_random=192, seed=1234):
-    rng = np.random.default_rng(seed)
-    edges = [0, 1, 2, 63, 64, 65, w.window - 2, w.window - 1, w.window, w.window + 1,
-             w.Lq // 2, w.Lq - 65, w.Lq - 64, w.Lq - 2, w.Lq - 1]
-    rows = set()
-    for i in edges:
-        if 0 <= i < w.Lq:
-            for b in range(w.B):
-                rows.add((b, int(rng.integers(w.Hq)), i))
-                rows.add((b, 0, i))
-                rows.add((b, w.Hq - 1, i))
-    while len(rows) < len(edges) * 2 + n_random:
-        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.Lq))))
-    return sorted(rows)
-
-
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
-def test_workload_parity(name):
+def test_workload_parity(name, oracle_pool):
     w = synth.WORKLOADS[name]
     announce(f"workload {name}")
     q, k, v = synth.draw_qkv(w)
@@ -47,16 +29,9 @@ def test_workload_parity(name):
     qf = synth.storage_to_f64(q, w.dtype)
     kf = synth.storage_to_f64(k, w.dtype)
     vf = synth.storage_to_f64(v, w.dtype)
-    if w.B * w.Hq * w.Lq * w.Lkv <= 64 * 1024 * 1024:
-        ref = oracle.attention(qf, kf, vf, w.causal, w.window, w.softcap)
-        ok, st = compare(got, ref)
-    else:
-        rows = _sample_rows(w)
-        ref = oracle.attention_rows(qf, kf, vf, rows, w.causal, w.window, w.softcap)
-        sel = np.stack([got[b, h, i] for (b, h, i) in rows])
-        ok, st = compare(sel, ref)
-        assert np.isfinite(got).all()
-    print(name, st, flush=True)
+    ref = oracle_pool.attention(qf, kf, vf, w.causal, w.window, w.softcap)
+    ok, st = compare(got, ref)
+    print(name, st, f"{got.size} elements compared", flush=True)
     assert ok, f"{name}: {st}"
     assert st["nrmse"] < 1e-2, f"{name}: {st}"
 
@@ -64,7 +39,7 @@ def test_workload_parity(name):
 # Shapes large enough (a workgroup per CU or more) that the plan picks the
 # prefill path -- the 8-wave, 256-row blocks for head sizes other than 128, and
 # for head size 128 the pipelined 4-wave, 128-row kernel that fills LDS with
-# direct global-to-LDS loads -- checked on sampled rows.
+# direct global-to-LDS loads -- checked on every element.
 LARGE_BLOCK_CASES = [
     # name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed
     ("lb_causal_window_cap_d128", 2, 32, 16, 2048, 2048, 128, True, 300, 20.0, "bf16", 201),
@@ -77,7 +52,7 @@ LARGE_BLOCK_CASES = [
 
 
 @pytest.mark.parametrize("case", LARGE_BLOCK_CASES, ids=lambda c: c[0])
-def test_large_block_parity(case):
+def test_large_block_parity(case, oracle_pool):
     from masked_gqa_attention_amd import _lib
     name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed = case
     rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), window, softcap,
@@ -93,13 +68,9 @@ def test_large_block_parity(case):
     qf = synth.storage_to_f64(q, dtype)
     kf = synth.storage_to_f64(k, dtype)
     vf = synth.storage_to_f64(v, dtype)
-    w = synth.Workload(name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap)
-    rows = _sample_rows(w.with_(window=max(window, 64)), n_random=160, seed=seed)
-    ref = oracle.attention_rows(qf, kf, vf, rows, causal, window, softcap)
-    sel = np.stack([got[b, h, i] for (b, h, i) in rows])
-    ok, st = compare(sel, ref)
-    assert np.isfinite(got).all()
-    print(name, st, flush=True)
+    ref = oracle_pool.attention(qf, kf, vf, causal, window, softcap)
+    ok, st = compare(got, ref)
+    print(name, st, f"{got.size} elements compared", flush=True)
     assert ok, f"{name}: {st}"
     assert st["nrmse"] < 1e-2, f"{name}: {st}"
 
