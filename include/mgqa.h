@@ -96,6 +96,28 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                 int causal, int window, float softcap, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest split workspace attn_fwd_noalloc serves from its device-resident
+ * scratch (8 MiB per GPU). */
+#define MGQA_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* attn_fwd_ex without any allocation and without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The split partials
+ * and arrival counters live in a device array inside the library, one per GPU
+ * (MGQA_NOALLOC_SCRATCH_BYTES, held until the process ends).  On the first call
+ * that needs it on a device, the library looks up that GPU's copy and clears
+ * its counter block with a kernel on `stream` (so the first such call on a
+ * device must not be under graph capture); later calls need no clearing,
+ * because every completed call leaves the counters at zero.  Plans whose
+ * workspace (attn_workspace_bytes) exceeds MGQA_NOALLOC_SCRATCH_BYTES return
+ * MGQA_ERR_WORKSPACE before any HIP call.  All calls on one GPU share the
+ * scratch: calls that can overlap on one GPU (different streams, or several
+ * host threads) race and must not be issued.  Same operation, dtypes, layouts,
+ * output bits and other errors as attn_fwd_ex. */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                     int B, int Hq, int Hkv, int Lq, int Lkv, int d,
+                     int causal, int window, float softcap, int dtype, void* stream);
+
 /* Attention over the first `length` keys of a KV cache of S slots per
  * (batch, kv head): K/V rows of head (b, g) start at element (b*Hkv + g)*S*d
  * ([B][Hkv][S][d], the layout kv_cache_append writes with layout 1).  Same

@@ -33,8 +33,10 @@ MGQA_FP16 = 1
 MGQA_F32 = 2
 
 # Every symbol the header declares.
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_cache", "attn_fwd_cache_append", "kv_cache_append",
-           "attn_workspace_bytes", "attn_plan", "attn_error_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_noalloc", "attn_fwd_cache", "attn_fwd_cache_append",
+           "kv_cache_append", "attn_workspace_bytes", "attn_plan", "attn_error_string", "attn_version")
+
+MGQA_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _lib = None
 
@@ -57,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd.restype = i
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_fwd_ex.restype = i
+    lib.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_noalloc.restype = i
     lib.attn_fwd_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_fwd_cache.restype = i
     lib.attn_fwd_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz,
@@ -89,6 +93,11 @@ def attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, d
                 workspace, workspace_bytes, stream) -> int:
     return load().attn_fwd_ex(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window),
                               float(softcap), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def attn_fwd_noalloc(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, stream) -> int:
+    return load().attn_fwd_noalloc(q, k, v, out, B, Hq, Hkv, Lq, Lkv, d, int(causal), int(window),
+                                   float(softcap), int(dtype), stream)
 
 
 def attn_fwd_cache(q, k_cache, v_cache, out, B, Hq, Hkv, Lq, S, length, ring_start, d, causal,

@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mgqa_internal.h"
 
 namespace mgqa {
@@ -248,6 +250,46 @@ static KernelArgs make_args(const Plan& p, const void* q, const void* k, const v
 
 using namespace mgqa;
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (attn_fwd_noalloc): the split
+// partials and arrival counters live in this file-scope device array instead
+// of a caller or library allocation.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` is only a handle
+// for the runtime: the device address of a GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MGQA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_err[kMaxDevices];
+
+// Device address of the current GPU's scratch; on first use on a device its
+// counter block is cleared on `stream` (the kernels leave the counters at zero
+// after every completed call, so later calls need no clearing).
+int scratch_for_current_device(void** out, void* stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MGQA_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev, stream] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      g_scratch_err[dev] = MGQA_ERR_HIP;
+      return;
+    }
+    if (launch_zero(ptr, kMaxCounters, stream) != hipSuccess) {
+      g_scratch_err[dev] = MGQA_ERR_HIP;
+      return;
+    }
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != MGQA_OK) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return MGQA_OK;
+}
+}  // namespace
+
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 extern "C" {
@@ -396,6 +438,25 @@ int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const floa
   if (launch_append(k_cache, v_cache, new_k, new_v, B, S, H, D, L, position, cache_dtype, layout,
                     length_out, stream) != hipSuccess)
     return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                     int Lq, int Lkv, int d, int causal, int window, float softcap, int dtype,
+                     void* stream) {
+  if (!q || !k || !v || !out) return MGQA_ERR_NULL;
+  Plan p;
+  const int err = make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, &p);
+  if (err) return err;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MGQA_ERR_ALIGN;
+  if (p.ws_bytes > MGQA_NOALLOC_SCRATCH_BYTES) return MGQA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    const int e = scratch_for_current_device(&ws, stream);
+    if (e != MGQA_OK) return e;
+  }
+  const KernelArgs a = make_args(p, q, k, v, out, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, ws);
+  if (launch(p, a, dtype, softcap > 0.f, stream) != hipSuccess) return MGQA_ERR_HIP;
   return MGQA_OK;
 }
 

@@ -294,3 +294,25 @@ def test_short_band_plan():
     P = ctypes.c_void_p(0x100000)
     rc = _lib.attn_fwd_cache(P, P, P, P, 1, 16, 16, 729, 729, 729, 5, 72, 0, 0, 0.0, 0, None, 0, None)
     assert rc == _lib.MGQA_ERR_UNSUPPORTED
+
+
+def test_noalloc_scratch_covers_every_plan():
+    """attn_fwd_noalloc serves split plans from a fixed device array: every
+    plan over a sweep of decode, multi-token and short shapes fits it, and
+    validation errors come before any HIP call."""
+    worst = 0
+    for B in (1, 8, 64):
+        for Hkv in (1, 2, 8):
+            for G in (1, 4, 16):
+                for Lq in (1, 4, 16, 48):
+                    for d in (64, 96, 128):
+                        for Lkv in (4096, 1 << 20):
+                            rc, info = _lib.attn_plan(B, G * Hkv, Hkv, Lq, Lkv, d, 1, 0, 0.0)
+                            if rc == 0:
+                                worst = max(worst, info["workspace_bytes"])
+    assert 0 < worst <= _lib.MGQA_NOALLOC_SCRATCH_BYTES
+    P = ctypes.c_void_p(0x100000)
+    assert _lib.attn_fwd_noalloc(None, P, P, P, 1, 4, 1, 1, 64, 128, 1, 0, 0.0, 0, None) == _lib.MGQA_ERR_NULL
+    assert _lib.attn_fwd_noalloc(P, P, P, P, 1, 4, 3, 1, 64, 128, 1, 0, 0.0, 0, None) == _lib.MGQA_ERR_SHAPE
+    assert _lib.attn_fwd_noalloc(P, P, P, ctypes.c_void_p(0x100008), 1, 4, 1, 1, 64, 128, 1, 0, 0.0, 0,
+                                 None) == _lib.MGQA_ERR_ALIGN
