@@ -1481,7 +1481,9 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
 //
 // With every score of its range in registers, a wave takes the row maximum
 // once and one exponential per score (two passes over registers): no running
-// maximum and no rescale.  Row sums come from the matrix cores (all-ones A
+// maximum and no rescale.  The code is straight-line over three steps for
+// every wave; steps past a wave's share have all keys masked (probability 0;
+// the V rows they multiply are other keys' rows, or zeros past Lkv).  Row sums come from the matrix cores (all-ones A
 // operand, the same 16-bit P as P.V).  The eight wave states then merge in
 // LDS in wave order; once a wave's P.V products are done, its region holds
 // its unnormalised rows (48 rows x DV*16 floats, exactly the region's bytes).
@@ -1505,6 +1507,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
   static_assert(NQB * 16 * OPITCH * 4 == REGION * 2, "a wave's output rows fill its V region exactly");
   __shared__ __attribute__((aligned(16))) uint16_t sv[NW * REGION];
   __shared__ float wm[NW][NQB * 16], wl[NW][NQB * 16];
+  __shared__ float wf[NW][NQB * 16];  // merge weight of each wave's rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -1555,13 +1558,21 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
   // Q^T operands: lane column c16 is the row, lane group g4 holds head-size
   // elements 32t + 8g4 .. +7 of step t.
   u32x4 qf[NQB][DQK];
-  int qpos[NQB];
+  int rlo[NQB], rspan[NQB];  // visible keys of this lane's row: [rlo, rlo + rspan]
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int r = 16 * qb + c16;
     const bool rok = r < nrows;
     const int pl = fdiv(r, a.div_g), hr = r - pl * G;
-    qpos[qb] = q0 + pl + off;
+    const int pos = q0 + pl + off;
+    int lo = 0, hi = a.Lkv - 1;
+    if (a.causal) hi = min(hi, pos);
+    if (a.window > 0) {
+      lo = max(0, pos - a.window + 1);
+      if (!a.causal) hi = min(hi, pos + a.window - 1);
+    }
+    rlo[qb] = lo;
+    rspan[qb] = hi - lo;
     const uint16_t* qrow = qg + (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + (rok ? q0 + pl : 0)) * d;
 #pragma unroll
     for (int t = 0; t < DQK; ++t) {
@@ -1570,54 +1581,71 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     }
   }
 
-  // K fragments of this wave's steps (registers) and its V rows (LDS), in
-  // step order so that the first step's scores wait for the least.
+  // K fragments of every step of this wave (registers) first, then its V rows
+  // (LDS): the scores wait for K only, and V lands while they are computed.
+  // Per-lane byte offsets are fixed; a step adds 32 rows through the
+  // instruction's scalar offset.  All NS steps are loaded whatever the wave's
+  // share (straight-line code, so the compiler counts the loads exactly);
+  // steps past the share read keys of the next range or zeros past Lkv and
+  // are never used.
+  const uint32_t step_bytes = 32u * (uint32_t)d * 2u;
   u32x4 kf[NS][2][DQK];
-  uint16_t* const myv = sv + wave * REGION;
+  {
+    uint32_t koff[2][DQK];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    if (st < my) {
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t krow = (uint32_t)(kw0 + 32 * st + 16 * hh + c16) * (uint32_t)d * 2u;
-#pragma unroll
-        for (int t = 0; t < DQK; ++t) {
-          const int col = 32 * t + 8 * g4;
-          const uint32_t vo = col < d ? krow + (uint32_t)col * 2u : kOutOfRange;
-          kf[st][hh][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)vo, 0, 0));
-        }
+      for (int t = 0; t < DQK; ++t) {
+        const int col = 32 * t + 8 * g4;
+        koff[hh][t] = col < d ? ((uint32_t)(kw0 + 16 * hh + c16) * (uint32_t)d + (uint32_t)col) * 2u : kOutOfRange;
       }
 #pragma unroll
-      for (int i = 0; i < VLOADS; ++i) {
-        const int n = 64 * i + lane;  // chunk n of the step's rows: row n / CPR, chunk n % CPR
-        const int row = n / CPR, ch = n - row * CPR;
-        const uint32_t vo =
-            ch * 8 < d ? ((uint32_t)(kw0 + 32 * st + row) * (uint32_t)d + (uint32_t)(ch * 8)) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs_v, (__attribute__((address_space(3))) void*)(myv + st * 32 * VPITCH + i * 512), 16, (int)vo, 0, 0,
-            0);
-      }
-    }
-  }
-
-  // ---- scores S^T = K Q^T of every step of the range -----------------------
-  f32x4 s[NS][2][NQB];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    if (st < my) {
+    for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < DQK; ++t)
+            kf[st][hh][t] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)koff[hh][t], (int)(st * step_bytes), 0));
+  }
+  // (Keeps the scheduler from sinking the K loads below the V loads.)
+  __builtin_amdgcn_sched_barrier(0);
+  uint16_t* const myv = sv + wave * REGION;
+  {
+    uint32_t voff[VLOADS];
 #pragma unroll
-          for (int t = 0; t < DQK; ++t) acc = Elem<T>::mfma(kf[st][hh][t], qf[qb][t], acc);
-          s[st][hh][qb] = acc;
-        }
+    for (int i = 0; i < VLOADS; ++i) {
+      const int n = 64 * i + lane;  // chunk n of a step's rows: row n / CPR, chunk n % CPR
+      const int row = n / CPR, ch = n - row * CPR;
+      voff[i] = ch * 8 < d ? ((uint32_t)(kw0 + row) * (uint32_t)d + (uint32_t)(ch * 8)) * 2u : kOutOfRange;
     }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs_v, (__attribute__((address_space(3))) void*)(myv + st * 32 * VPITCH + i * 512), 16, (int)voff[i],
+              (int)(st * step_bytes), 0, 0);
   }
 
-  // ---- mask (steps crossing a band edge or the end of the keys) ------------
+  // ---- scores S^T = K Q^T of every step ------------------------------------
+  // Straight-line over all NS steps; steps past this wave's share are masked
+  // out below.
+  f32x4 s[NS][2][NQB];
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < DQK; ++t) acc = Elem<T>::mfma(kf[st][hh][t], qf[qb][t], acc);
+        s[st][hh][qb] = acc;
+      }
+
+  // ---- mask: steps crossing a band edge or the end of the keys, and steps
+  // past this wave's share (all keys) ------------------------------------------
   bool part[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
@@ -1628,16 +1656,24 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
       full = full && (pos_max - k0 < a.window);
       if (!a.causal) full = full && (k0 + 31 - pos_min < a.window);
     }
-    part[st] = st < my && !full;
-    if (part[st]) {
+    const bool mine = st < my;
+    part[st] = !mine || !full;
+    if (!mine) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+        for (int qb = 0; qb < NQB; ++qb) s[st][hh][qb] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    } else if (part[st]) {
+      // key j is visible to the row iff (unsigned)(j - lo) <= span
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int ub = k0 + 4 * g4 - rlo[qb];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (!key_visible(k0 + 16 * hh + 4 * g4 + i, qpos[qb], a.Lkv, a.causal, a.window))
-              s[st][hh][qb][i] = kNegInf;
+            if ((unsigned)(ub + 16 * hh + i) > (unsigned)rspan[qb]) s[st][hh][qb][i] = kNegInf;
+      }
     }
   }
 
@@ -1650,11 +1686,10 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     float mx = kNegInf;
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      if (st < my)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][hh][qb][i]);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][hh][qb][i]);
     mx = col_max(mx);
     if (SOFTCAP)
       m_e[qb] = (mx == kNegInf) ? kNegInf
@@ -1671,28 +1706,26 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     const float mref = (m_e[qb] == kNegInf) ? 0.f : m_e[qb];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      if (st < my) {
-        float p[8];
+      float p[8];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = s[st][hh][qb][i];
-            float pv;
-            if (SOFTCAP) {
-              // c*tanh(u) = c - 2c/(exp(2u)+1), in base-2 exponent units.
-              const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
-              pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
-              if (part[st] && x == kNegInf) pv = 0.f;
-            } else {
-              pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
-            }
-            p[hh * 4 + i] = pv;
+        for (int i = 0; i < 4; ++i) {
+          const float x = s[st][hh][qb][i];
+          float pv;
+          if (SOFTCAP) {
+            // c*tanh(u) = c - 2c/(exp(2u)+1), in base-2 exponent units.
+            const float r = fast_rcp(fast_exp2(x * a.gamma) + 1.0f);
+            pv = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
+            if (part[st] && x == kNegInf) pv = 0.f;
+          } else {
+            pv = fast_exp2(__builtin_fmaf(x, a.alpha, -mref));
           }
-        pk[st][qb] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]), Elem<T>::pack2(p[4], p[5]),
-                           Elem<T>::pack2(p[6], p[7])};
-        ls[qb] = Elem<T>::mfma(ones, pk[st][qb], ls[qb]);
-      }
+          p[hh * 4 + i] = pv;
+        }
+      pk[st][qb] = u32x4{Elem<T>::pack2(p[0], p[1]), Elem<T>::pack2(p[2], p[3]), Elem<T>::pack2(p[4], p[5]),
+                         Elem<T>::pack2(p[6], p[7])};
+      ls[qb] = Elem<T>::mfma(ones, pk[st][qb], ls[qb]);
     }
   }
 
@@ -1706,16 +1739,14 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     for (int db = 0; db < DV; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    if (st < my) {
-      const uint16_t* v0 = myv + (32 * st + 4 * g4 + (c16 >> 2)) * VPITCH + 4 * (c16 & 3);
+    const uint16_t* v0 = myv + (32 * st + 4 * g4 + (c16 >> 2)) * VPITCH + 4 * (c16 & 3);
 #pragma unroll
-      for (int db = 0; db < DV; ++db) {
-        const u32x2 lo = lds_read_tr4(v0 + 16 * db);
-        const u32x2 hi = lds_read_tr4(v0 + 16 * VPITCH + 16 * db);
-        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+    for (int db = 0; db < DV; ++db) {
+      const u32x2 lo = lds_read_tr4(v0 + 16 * db);
+      const u32x2 hi = lds_read_tr4(v0 + 16 * VPITCH + 16 * db);
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[st][qb], o[qb][db]);
-      }
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[st][qb], o[qb][db]);
     }
   }
 
@@ -1733,6 +1764,21 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
       *reinterpret_cast<f32x4*>(&wo[(16 * qb + c16) * OPITCH + 16 * db + 4 * g4]) = o[qb][db];
   }
   __syncthreads();
+  // Weight of wave w's row r: 2^(m_w - M) / L with M the row's maximum over
+  // the waves and L = sum_w 2^(m_w - M) l_w (each sum in wave order); one
+  // thread per (row, wave).
+  static_assert(NQB * 16 * NW <= 64 * NW, "one thread per (row, wave)");
+  if (tid < NQB * 16 * NW) {
+    const int r = tid / NW, w = tid - r * NW;
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) M = fmaxf(M, wm[u][r]);
+    float L = 0.f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) L += (wm[u][r] == kNegInf ? 0.f : fast_exp2(wm[u][r] - M)) * wl[u][r];
+    wf[w][r] = (wm[w][r] == kNegInf) ? 0.f : fast_exp2(wm[w][r] - M) / L;
+  }
+  __syncthreads();
   constexpr int C4 = DV * 4;  // float4 chunks of one output row
   constexpr int JN = (NQB * 16 * C4 + 64 * NW - 1) / (64 * NW);
 #pragma unroll
@@ -1740,22 +1786,14 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     const int q = tid + j * 64 * NW;
     const int r = q / C4, c4 = q - r * C4;
     if (q >= NQB * 16 * C4 || r >= nrows || 4 * c4 >= d) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][r]);
-    float L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = wm[w][r] == kNegInf ? 0.f : fast_exp2(wm[w][r] - M);
-      L += f * wl[w][r];
-      acc += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(sv + w * REGION) + r * OPITCH + 4 * c4);
-    }
-    const float inv = 1.0f / L;
+    for (int w = 0; w < NW; ++w)
+      acc += wf[w][r] * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(sv + w * REGION) + r * OPITCH +
+                                                      4 * c4);
     const int pr = fdiv(r, a.div_g);
     const size_t oo = (((size_t)b * a.Hq + kvh * G + (r - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
-    *reinterpret_cast<u32x2*>(og + oo) =
-        u32x2{Elem<T>::pack2(acc[0] * inv, acc[1] * inv), Elem<T>::pack2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(og + oo) = u32x2{Elem<T>::pack2(acc[0], acc[1]), Elem<T>::pack2(acc[2], acc[3])};
   }
 }
 
