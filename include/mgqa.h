@@ -203,9 +203,18 @@ int kv_cache_append(void* k_cache, void* v_cache, const float* new_k, const floa
  * info[8] column slices: workgroups sharing one key range of a block of rows,
  *         each computing P.V for its share of the head size (1, or 2 when a
  *         single 16-row block has many key splits; split path only)
+ * info[9..11] work items of the head-size-128 prefill kernel (0 otherwise).
+ *         Per (batch row, kv head) there are n blocks of info[2]/G
+ *         positions and info[1]/(B*Hkv) workgroups: the first
+ *         ceil(info[10]/2) each run blocks info[10]-1-j and j one after the
+ *         other (the short-band ramp under a causal mask, ends paired; one
+ *         block when the two coincide), the next info[11] one whole block
+ *         each (n-1 downwards), the rest one half block each (the next
+ *         blocks downwards, two halves of info[2]/(2G) positions apiece).
+ *         info[9] = ceil(info[10]/2).
  * Returns 0 or a validation error code (then info is untouched). */
 int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d,
-              int causal, int window, float softcap, int dtype, long long info[9]);
+              int causal, int window, float softcap, int dtype, long long info[12]);
 
 /* Static text for an error code (never NULL). */
 const char* attn_error_string(int code);

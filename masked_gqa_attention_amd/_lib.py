@@ -127,7 +127,7 @@ def attn_workspace_bytes(B, Hq, Hkv, Lq, Lkv, d, causal, window) -> int:
 
 
 PLAN_FIELDS = ("path", "workgroups", "rows_per_wg", "nsplit", "keys_per_tile", "d_qk_pad",
-               "d_pv_pad", "workspace_bytes", "ncol")
+               "d_pv_pad", "workspace_bytes", "ncol", "pf_pairs", "pf_ramp", "pf_full")
 
 
 def attn_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype=MGQA_BF16):

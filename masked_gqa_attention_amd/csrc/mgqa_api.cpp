@@ -8,7 +8,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <functional>
 #include <mutex>
+#include <vector>
 
 #include "mgqa_internal.h"
 
@@ -65,6 +68,189 @@ static void block_band(int q0, int m_eff, int Lq, int Lkv, int causal, int windo
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work items of the pipelined head-size-128 prefill kernel.  A launch runs in
+// rounds of 512 workgroups (two per CU); its length is set by the last round.
+// Under a causal mask the first position blocks (the ramp) have shorter key
+// bands than the rest; taken last first they leave a last round of short
+// blocks that finishes long after the average.  Two remedies, chosen by a
+// model of the launch: the two ends of the ramp paired into one workgroup
+// (blocks R-1-j and j: about one full band together), and the last round
+// filled with half blocks (64 rows) instead of part-filled with whole ones.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Model of a launch, in 32-key steps of a 128-row block taken by one of two
+// workgroups sharing a CU.  A block costs kPipeSetupSteps of set-up (Q loads,
+// the first tiles' round trip, the output) plus one step per tile of its
+// band; a 64-row half block kPipeHalfStep per tile.  A workgroup alone on
+// its CU runs kPipeAloneSpeed times faster.  (Fitted to timings of causal and
+// windowed prefill launches on MI355X.)
+constexpr double kPipeSetupSteps = 4.0;
+constexpr double kPipeHalfStep = 0.7;
+constexpr double kPipeAloneSpeed = 1.6;
+constexpr int kXCDs = 8;
+constexpr int kCUsPerXCD = kCUs / kXCDs;
+constexpr long long kPipeMaxModeled = 1 << 18;  // larger grids keep the plain order
+
+struct PipeSched {
+  int items, pairs, ramp, full;
+};
+
+int band_tiles(int q0, int m, int Lq, int Lkv, int causal, int window) {
+  int lo, hi;
+  block_band(q0, Lq - q0 < m ? Lq - q0 : m, Lq, Lkv, causal, window, &lo, &hi);
+  return hi / kPipe4Keys - lo / kPipe4Keys + 1;
+}
+
+// Modeled length of the launch.  Every XCD starts its workgroups in order,
+// each on the least occupied of its CUs that has room (two per CU).  With a
+// grid that is a multiple of 8 the kernel gives XCD x the x-th eighth of the
+// (unit, item) list; otherwise the hardware deals workgroup i to XCD i % 8.
+double pipe_makespan(const PipeSched& s, long long units, const std::vector<int>& tiles, int m, int Lq,
+                     int Lkv, int causal, int window) {
+  const int n = (int)tiles.size();
+  std::vector<double> cost(s.items);
+  for (int j = 0; j < s.items; ++j) {
+    if (j < s.pairs) {
+      const int hi = s.ramp - 1 - j;
+      cost[j] = kPipeSetupSteps + tiles[hi] + (j < hi ? kPipeSetupSteps + tiles[j] : 0.0);
+    } else if (j < s.pairs + s.full) {
+      cost[j] = kPipeSetupSteps + tiles[n - 1 - (j - s.pairs)];
+    } else {
+      const int h = j - s.pairs - s.full, pb = n - 1 - s.full - (h >> 1);
+      const int q0 = pb * m + (h & 1) * (m / 2);
+      cost[j] = kPipeSetupSteps + kPipeHalfStep * band_tiles(q0, m / 2, Lq, Lkv, causal, window);
+    }
+  }
+  const long long nwg = units * s.items;
+  const bool renumbered = nwg % kXCDs == 0;
+  double worst = 0.0;
+  double rem[kCUsPerXCD][2];  // work left in each slot (0: free)
+  int busy[kCUsPerXCD];
+  for (int x = 0; x < kXCDs; ++x) {
+    const long long first = renumbered ? x * (nwg / kXCDs) : x;
+    const long long stop = renumbered ? (x + 1) * (nwg / kXCDs) : nwg;
+    const long long stride = renumbered ? 1 : kXCDs;
+    for (int c = 0; c < kCUsPerXCD; ++c) rem[c][0] = rem[c][1] = 0.0, busy[c] = 0;
+    long long next = first;
+    double t = 0.0;
+    int running = 0;
+    while (true) {
+      // Start workgroups while a CU has room: empty CUs first.
+      while (next < stop) {
+        int best = -1;
+        for (int c = 0; c < kCUsPerXCD && best < 0; ++c)
+          if (busy[c] == 0) best = c;
+        for (int c = 0; c < kCUsPerXCD && best < 0; ++c)
+          if (busy[c] == 1) best = c;
+        if (best < 0) break;
+        const int slot = rem[best][0] > 0.0 ? 1 : 0;
+        rem[best][slot] = cost[next % s.items];
+        ++busy[best];
+        ++running;
+        next += stride;
+      }
+      if (running == 0) break;
+      // Advance to the next completion.
+      double dt = 1e300;
+      for (int c = 0; c < kCUsPerXCD; ++c) {
+        const double speed = busy[c] == 1 ? kPipeAloneSpeed : 1.0;
+        for (int k = 0; k < 2; ++k)
+          if (rem[c][k] > 0.0) dt = std::min(dt, rem[c][k] / speed);
+      }
+      t += dt;
+      for (int c = 0; c < kCUsPerXCD; ++c) {
+        const double speed = busy[c] == 1 ? kPipeAloneSpeed : 1.0;
+        for (int k = 0; k < 2; ++k)
+          if (rem[c][k] > 0.0) {
+            rem[c][k] -= dt * speed;
+            if (rem[c][k] <= 1e-9) {
+              rem[c][k] = 0.0;
+              --busy[c];
+              --running;
+            }
+          }
+      }
+    }
+    worst = std::max(worst, t);
+    if (renumbered && units % kXCDs == 0) break;  // every XCD runs the same list
+  }
+  return worst;
+}
+
+PipeSched pipe_schedule_uncached(long long units, int n, int m, int Lq, int Lkv, int causal, int window) {
+  const PipeSched plain = {n, 0, 0, n};
+  if (units * n > kPipeMaxModeled) return plain;
+  std::vector<int> tiles(n);
+  int tmax = 0;
+  for (int pb = 0; pb < n; ++pb) {
+    tiles[pb] = band_tiles(pb * m, m, Lq, Lkv, causal, window);
+    tmax = std::max(tmax, tiles[pb]);
+  }
+  // Ramp: the leading blocks whose band is shorter than the longest by two
+  // tiles or more (bands of the full blocks differ by one tile with their
+  // alignment).
+  int ramp = 0;
+  if (causal)
+    while (ramp < n && tiles[ramp] < tmax - 1) ++ramp;
+  // The last block, when partial, is never halved: its second half could be
+  // empty.
+  const int keep = (Lq % m != 0) ? 1 : 0;
+  PipeSched best = plain;
+  double best_t = pipe_makespan(plain, units, tiles, m, Lq, Lkv, causal, window);
+  const double plain_t = best_t;
+  // Without pairs (r = 0), and with the ramp's ends paired (r = ramp).
+  // Candidates: the ramp's ends paired (r = ramp) or not (r = 0), each with
+  // no half blocks, with as many as turn the part-filled last round of whole
+  // blocks into a round of halves, and (without pairs) every block halved.
+  const int nr = ramp >= 2 ? 2 : 1;
+  for (int c = 0; c < nr; ++c) {
+    const int r = c ? ramp : 0;
+    const int pairs = (r + 1) / 2;
+    const int blocks = n - r;  // whole blocks past the ramp
+    const int hmax = (m % 2 == 0) ? blocks - keep : 0;
+    auto eval = [&](int H) {
+      if (H < 0 || H > hmax || (r == 0 && H == 0)) return;  // (r, H) = (0, 0) is the plain order
+      const PipeSched s = {pairs + blocks + H, pairs, r, blocks - H};
+      const double t = pipe_makespan(s, units, tiles, m, Lq, Lkv, causal, window);
+      if (t < best_t) {
+        best_t = t;
+        best = s;
+      }
+    };
+    eval(0);
+    const long long round = 2LL * kCUs;
+    const long long rest = (units * (pairs + blocks)) % round;
+    if (rest > 0) eval((int)((rest + units - 1) / units));
+    if (r == 0 && units * blocks <= round) eval(hmax);
+  }
+  // Keep the plain order unless the model gains at least 2%.
+  return best_t < 0.98 * plain_t ? best : plain;
+}
+
+PipeSched pipe_schedule(long long units, int n, int m, int Lq, int Lkv, int causal, int window) {
+  // A few recent shapes per thread: repeated calls of one shape plan once.
+  constexpr int kMemo = 8;
+  struct Entry {
+    long long key[7];
+    PipeSched s;
+  };
+  thread_local Entry memo[kMemo];
+  thread_local int filled = 0, next = 0;
+  const long long k[7] = {units, n, m, Lq, Lkv, causal, window};
+  for (int i = 0; i < filled; ++i)
+    if (std::equal(k, k + 7, memo[i].key)) return memo[i].s;
+  Entry& e = memo[next];
+  std::copy(k, k + 7, e.key);
+  e.s = pipe_schedule_uncached(units, n, m, Lq, Lkv, causal, window);
+  next = (next + 1) % kMemo;
+  if (filled < kMemo) ++filled;
+  return e.s;
+}
+
+}  // namespace
+
 int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
               float softcap, int dtype, Plan* plan) {
   const int err = validate(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype);
@@ -93,7 +279,14 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
     p.rows_per_wg = 16 * p.nwaves * p.nqb;
     p.m = m_big;
     p.n_pos_blk = (Lq + m_big - 1) / m_big;
-    p.workgroups = wgs_big;
+    PipeSched s = {p.n_pos_blk, 0, 0, p.n_pos_blk};
+    if (d128) s = pipe_schedule(units, p.n_pos_blk, p.m, Lq, Lkv, causal, window);
+    p.pf_items = s.items;
+    p.pf_pairs = s.pairs;
+    p.pf_ramp = s.ramp;
+    p.pf_full = s.full;
+    p.workgroups = units * s.items;
+    if (p.workgroups >= (1LL << 31)) return MGQA_ERR_RANGE;
     *plan = p;
     return MGQA_OK;
   }
@@ -237,6 +430,11 @@ static KernelArgs make_args(const Plan& p, const void* q, const void* k, const v
   a.nwg = (int)p.workgroups;
   a.tiles_per_split = p.tiles_per_split;
   a.nrows = p.m * a.G;
+  a.pf_items = p.pf_items;
+  a.pf_pairs = p.pf_pairs;
+  a.pf_ramp = p.pf_ramp;
+  a.pf_full = p.pf_full;
+  a.div_items = make_fastdiv((uint32_t)(p.pf_items > 0 ? p.pf_items : 1));
   if (ws) {
     char* base = static_cast<char*>(ws);
     a.ws_cnt = reinterpret_cast<unsigned*>(base + p.ws_cnt_off);
@@ -294,7 +492,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 extern "C" {
 
-int attn_version(void) { return 102; }
+int attn_version(void) { return 103; }
 
 const char* attn_error_string(int code) {
   switch (code) {
@@ -316,7 +514,7 @@ const char* attn_error_string(int code) {
 }
 
 int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
-              float softcap, int dtype, long long info[9]) {
+              float softcap, int dtype, long long info[12]) {
   if (!info) return MGQA_ERR_NULL;
   Plan p;
   const int err = make_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, &p);
@@ -330,6 +528,10 @@ int attn_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   info[6] = p.dv * 16;
   info[7] = (long long)p.ws_bytes;
   info[8] = p.ncol > 0 ? p.ncol : 1;
+  const bool items = p.path == kPathPrefill && d == 128;
+  info[9] = items ? p.pf_pairs : 0;
+  info[10] = items ? p.pf_ramp : 0;
+  info[11] = items ? p.pf_full : 0;
   return MGQA_OK;
 }
 

@@ -84,6 +84,11 @@ struct KernelArgs {
   const float* app_k;
   const float* app_v;
   int app_pos, app_len;
+  // Pipelined head-size-128 prefill: pf_items work items per unit -- pf_pairs
+  // pairs of the first pf_ramp position blocks, pf_full whole blocks, then
+  // half blocks (two items each).
+  int pf_items, pf_pairs, pf_ramp, pf_full;
+  FastDiv div_items;  // for pf_items
 };
 
 struct Plan {
@@ -100,6 +105,7 @@ struct Plan {
   int nsplit;
   int tiles_per_split;
   int ncol;           // split path: workgroups sharing one key range, each with 1/ncol of V's columns
+  int pf_items, pf_pairs, pf_ramp, pf_full;  // pipelined prefill work items (see KernelArgs)
   long long workgroups;
   size_t ws_bytes;
   size_t ws_o_off, ws_ml_off, ws_cnt_off;

@@ -686,11 +686,12 @@ struct PipeAddr {
   int va[8];
 };
 
-// Probabilities of 4 scores (one 16-key half of one 16-row block), fp32.
-template <bool SOFTCAP>
+// Probabilities of scores I0 .. I0+N-1 of 4 (one 16-key half of one 16-row
+// block), fp32.
+template <bool SOFTCAP, int I0 = 0, int N = 4>
 __device__ __forceinline__ void pipe_probs(const f32x4& x, float mref, const KernelArgs& a, float (&p)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = I0; i < I0 + N; ++i) {
     if (SOFTCAP) {
       const float r = fast_rcp(fast_exp2(x[i] * a.gamma) + 1.0f);
       p[i] = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
@@ -712,28 +713,32 @@ __device__ __forceinline__ void pin(f32x4& v) { asm volatile("" : "+v"(v)); }
 // (unsigned)(ubase[qb] + 16*hh + i) <= span[qb]; MASK is false when every
 // key of the step is visible to every row of the workgroup.
 //
-// The products and the exponentials form one straight-line block of four
-// quarters, each with 8 MFMAs (two V and two K fragments) and the
-// probabilities of 4 scores, so that few fragments are live at a time.  The
+// NQB 16-row blocks per wave (2, or 1 for half-height blocks).  The products
+// and the exponentials form one straight-line block of four quarters, each
+// with 4*NQB MFMAs (two V and two K fragments) and the probabilities of 2*NQB
+// scores, so that few fragments are live at a time.  The
 // mask (partial steps only) is applied after that block.  With a running
 // maximum, the new maximum is taken first (the exponentials use it at once)
 // and the accumulators are rescaled at the end, after the products of step
 // j-1 -- whose probabilities used the old maximum -- are in.
-template <typename T, bool SOFTCAP, bool FIXREF, int KOFF, int VOFF>
+template <typename T, int NQB, bool SOFTCAP, bool FIXREF, int KOFF, int VOFF>
 __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const uint16_t* Vst, const PipeAddr& ad,
-                                          f32x4 (&sc)[2][2], f32x4 (&sn)[2][2],
-                                          const u32x4 (&pp)[2], u32x4 (&pc)[2], const u32x4 (&qf)[2][4],
-                                          f32x4 (&o)[2][8], f32x4 (&ls)[2], float (&m_e)[2],
-                                          const int (&ubase)[2], const int (&span)[2], const KernelArgs& a) {
+                                          f32x4 (&sc)[NQB][2], f32x4 (&sn)[NQB][2],
+                                          const u32x4 (&pp)[NQB], u32x4 (&pc)[NQB], const u32x4 (&qf)[NQB][4],
+                                          f32x4 (&o)[NQB][8], f32x4 (&ls)[NQB], float (&m_e)[NQB],
+                                          const int (&ubase)[NQB], const int (&span)[NQB], const KernelArgs& a) {
   const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
                       OnesOperand<T>::kPair};
-  float mref[2], resc[2] = {1.0f, 1.0f};
+  float mref[NQB], resc[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) resc[qb] = 1.0f;
   if constexpr (FIXREF) {
-    mref[0] = mref[1] = a.c2 - 64.0f;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) mref[qb] = a.c2 - 64.0f;
   } else {
     if (mask) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -741,7 +746,7 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
             if ((unsigned)(ubase[qb] + 16 * hh + i) > (unsigned)span[qb]) sc[qb][hh][i] = kNegInf;
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       float mx = fmaxf(fmaxf(fmaxf(sc[qb][0][0], sc[qb][0][1]), fmaxf(sc[qb][0][2], sc[qb][0][3])),
                        fmaxf(fmaxf(sc[qb][1][0], sc[qb][1][1]), fmaxf(sc[qb][1][2], sc[qb][1][3])));
       mx = col_max(mx);
@@ -774,38 +779,51 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
       kf[e] = *reinterpret_cast<const u32x4*>(Kst + ad.ka[t0 + e] + KOFF + hh * 16 * 128);
     }
   };
-  float p[2][2][4];
+  float p[NQB][2][4];
   u32x4 fr[2][2][2];  // [buffer][V, K][e]
   frags(0, fr[0][0], fr[0][1]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int hh = k >> 1, t0 = 2 * (k & 1);
-    const int qs = k >> 1, hs = k & 1;  // scores whose probabilities this quarter computes
+    // Scores whose probabilities this quarter computes: of block qs, half hs
+    // (two row blocks: all four of a half per quarter; one row block: two).
+    constexpr bool TWO = NQB == 2;
+    const int qs = TWO ? (k >> 1) : 0, hs = TWO ? (k & 1) : (k >> 1);
     const int cur = k & 1;
     pin(sc[qs][hs]);
     if (k < 3) frags(k + 1, fr[cur ^ 1][0], fr[cur ^ 1][1]);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[qb][2 * k + e] = Elem<T>::mfma(fr[cur][0][e], pp[qb], o[qb][2 * k + e]);
+      for (int qb = 0; qb < NQB; ++qb) o[qb][2 * k + e] = Elem<T>::mfma(fr[cur][0][e], pp[qb], o[qb][2 * k + e]);
     if (k == 3) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) ls[qb] = Elem<T>::mfma(ones, pp[qb], ls[qb]);
+      for (int qb = 0; qb < NQB; ++qb) ls[qb] = Elem<T>::mfma(ones, pp[qb], ls[qb]);
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       f32x4 acc = (k & 1) ? sn[qb][hh] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 2; ++e) acc = Elem<T>::mfma(fr[cur][1][e], qf[qb][t0 + e], acc);
       sn[qb][hh] = acc;
     }
-    pipe_probs<SOFTCAP>(sc[qs][hs], mref[qs], a, p[qs][hs]);
+    if constexpr (TWO) {
+      pipe_probs<SOFTCAP>(sc[qs][hs], mref[qs], a, p[qs][hs]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pin(p[qs][hs][i]);
+      for (int i = 0; i < 4; ++i) pin(p[qs][hs][i]);
+    } else if (k & 1) {
+      pipe_probs<SOFTCAP, 2, 2>(sc[qs][hs], mref[qs], a, p[qs][hs]);
+      pin(p[qs][hs][2]);
+      pin(p[qs][hs][3]);
+    } else {
+      pipe_probs<SOFTCAP, 0, 2>(sc[qs][hs], mref[qs], a, p[qs][hs]);
+      pin(p[qs][hs][0]);
+      pin(p[qs][hs][1]);
+    }
     // Next quarter's fragment reads first, then one MFMA per three vector-ALU ops.
     if (k < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int g = 0; g < 10; ++g) {
+    for (int g = 0; g < 5 * NQB; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
@@ -814,7 +832,7 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
 
   if (mask) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -822,13 +840,13 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
           if ((unsigned)(ubase[qb] + 16 * hh + i) > (unsigned)span[qb]) p[qb][hh][i] = 0.f;
   }
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQB; ++qb)
     pc[qb] = u32x4{Elem<T>::pack2(p[qb][0][0], p[qb][0][1]), Elem<T>::pack2(p[qb][0][2], p[qb][0][3]),
                    Elem<T>::pack2(p[qb][1][0], p[qb][1][1]), Elem<T>::pack2(p[qb][1][2], p[qb][1][3])};
 
   if constexpr (!FIXREF) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
       if (resc[qb] != 1.0f) {
         ls[qb] *= resc[qb];
 #pragma unroll
@@ -839,40 +857,25 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
 
 // ---------------------------------------------------------------------------
 // The pipelined prefill kernel for head size 128 (layout and schedule above).
+//
+// pipe4_block: one block of 64*NQB rows -- query positions q0 .. q0+m_item-1
+// of unit `unit` (batch row * Hkv + kv head), every head of the group, head
+// fastest -- through its whole key band.  A workgroup that runs two blocks
+// places a barrier between them: the second block's first loads overwrite
+// stages the first block's last steps read.
 // ---------------------------------------------------------------------------
-template <typename T, bool SOFTCAP, bool FIXREF>
-__global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
+template <typename T, int NQB, bool SOFTCAP, bool FIXREF>
+__device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem, int unit, int q0, int m_item) {
   constexpr int NWAVES = 4, D = 128, KEYS = 32, TILE = kPipe4Tile, NS = kPipe4Stages;
   constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row direct-to-LDS loads per wave per tensor
   static_assert(IPW == 2, "the wait counts below assume two loads per tensor per wave");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NS * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
-
-  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
-  // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
-  // range of (unit, position block) pairs: the blocks of one unit then share
-  // their K/V tiles in one L2.
-  // Within a unit the blocks are taken last first: under a causal mask the
-  // later blocks have the longer key bands, and starting the longest work
-  // first leaves shorter blocks to even out the end of the launch.
-  // Every argument the first loads depend on, asked for at once, so that
-  // their loads leave in one batch and cost one round trip.
-  asm volatile("" : : "s"(a.kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
-               "s"(a.G), "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.causal), "s"(a.window), "s"(a.div_g.m),
-               "s"(a.div_g.s), "s"(a.div_npos.m), "s"(a.div_npos.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s),
-               "s"(a.nwg));
-  const int bid = blockIdx.x;
-  int lin = bid;
-  if ((a.nwg & 7) == 0) lin = (bid & 7) * (a.nwg >> 3) + (bid >> 3);
-  const int unit = fdiv(lin, a.div_npos);  // b * Hkv + kvh
-  const int pblk = a.n_pos_blk - 1 - (lin - unit * a.n_pos_blk);
   const int b = fdiv(unit, a.div_hkv), kvh = unit - b * a.Hkv;
   const int G = a.G;
-  const int q0 = pblk * a.m;
-  const int m_eff = min(a.m, a.Lq - q0);
+  const int m_eff = min(m_item, a.Lq - q0);
   const int off = a.Lkv - a.Lq;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
@@ -892,11 +895,11 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 
   // Q first: the direct-to-LDS loads are counted after it, so waiting for
   // the first tile also waits for Q.
-  u32x4 qf[2][4];
-  int rconst[2], span[2];
+  u32x4 qf[NQB][4];
+  int rconst[NQB], span[NQB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = (wave * 2 + qb) * 16 + c16;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int r = (wave * NQB + qb) * 16 + c16;
     const int pl = fdiv(r, a.div_g), hr = r - pl * G;
     const bool ok = pl < m_eff;
     const int pos = q0 + pl + off;
@@ -967,12 +970,13 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
 
-  float m_e[2] = {kNegInf, kNegInf};
-  f32x4 o[2][8], ls[2];
-  f32x4 sa[2][2], sb[2][2];
-  u32x4 pa[2], pb[2];
+  float m_e[NQB];
+  f32x4 o[NQB][8], ls[NQB];
+  f32x4 sa[NQB][2], sb[NQB][2];
+  u32x4 pa[NQB], pb[NQB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_e[qb] = kNegInf;
     ls[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     pb[qb] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -980,7 +984,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   }
   // Scores of the first step (stage 0).
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1003,7 +1007,8 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   // tile t+1 (stage ST+1; discarded after the last tile), P.V of tile t-1
   // (stage ST-1).  Before it: tile t+1 landed, and every wave past step t-1.
   // sc/sn/pp/pc alternate between the two register sets from step to step.
-  auto step = [&](auto stc, int t, f32x4 (&sc)[2][2], f32x4 (&sn)[2][2], const u32x4 (&pp)[2], u32x4 (&pc)[2]) {
+  auto step = [&](auto stc, int t, f32x4 (&sc)[NQB][2], f32x4 (&sn)[NQB][2], const u32x4 (&pp)[NQB],
+                  u32x4 (&pc)[NQB]) {
     constexpr int ST = decltype(stc)::value;
     constexpr int SP = (ST + NS - 1) % NS, SN = (ST + 1) % NS;
     if (t > t_begin) {
@@ -1018,9 +1023,11 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
     // Tile t-2's stage is free: every wave is past step t-1, its last reader.
     if (t + 3 < t_end) fetch(t + 3, (ST + 3) % NS);
     const int kg0 = t * KEYS;
-    const int ub[2] = {kg0 + rconst[0], kg0 + rconst[1]};
-    pipe_step<T, SOFTCAP, FIXREF, SN * TILE, SP * TILE>(!step_full(kg0), sk, sv, ad, sc, sn, pp, pc, qf, o, ls, m_e,
-                                                        ub, span, a);
+    int ub[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) ub[qb] = kg0 + rconst[qb];
+    pipe_step<T, NQB, SOFTCAP, FIXREF, SN * TILE, SP * TILE>(!step_full(kg0), sk, sv, ad, sc, sn, pp, pc, qf, o,
+                                                             ls, m_e, ub, span, a);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -1056,8 +1063,9 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   {
     const u32x4 ones = {OnesOperand<T>::kPair, OnesOperand<T>::kPair, OnesOperand<T>::kPair,
                         OnesOperand<T>::kPair};
-    const u32x4* pl = (last & 1) ? pb : pa;
-    u32x4 pfin[2] = {pl[0], pl[1]};
+    u32x4 pfin[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) pfin[qb] = (last & 1) ? pb[qb] : pa[qb];
     const int vst = (last % NS) * TILE;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
@@ -1066,20 +1074,71 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
       const u32x2 hi = lds_read_tr4(v0 + 16 * 128);
       const u32x4 v1 = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[qb][db] = Elem<T>::mfma(v1, pfin[qb], o[qb][db]);
+      for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(v1, pfin[qb], o[qb][db]);
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) ls[qb] = Elem<T>::mfma(ones, pfin[qb], ls[qb]);
+    for (int qb = 0; qb < NQB; ++qb) ls[qb] = Elem<T>::mfma(ones, pfin[qb], ls[qb]);
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = (wave * 2 + qb) * 16 + c16;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int r = (wave * NQB + qb) * 16 + c16;
     const int pl = fdiv(r, a.div_g), hr = r - pl * G;
     if (pl < m_eff) {
       const size_t ro = (((size_t)b * a.Hq + kvh * G + hr) * a.Lq + q0 + pl) * D;
       store_row<T, 8>(og + ro, o[qb], 1.0f / ls[qb][0], D, g4);
     }
+  }
+}
+
+// Work items of one unit, in launch order (item j; n = n_pos_blk blocks of m
+// positions, R = pf_ramp):
+//   j <  pf_pairs:             blocks R-1-j and j, one after the other (one
+//                              block when the two coincide);
+//   j <  pf_pairs + pf_full:   block n-1-(j-pf_pairs) (whole blocks, last first);
+//   otherwise:                 the halves (m/2 positions, one 16-row block per
+//                              wave) of the remaining blocks, two items each.
+// Under a causal mask the first R blocks have shorter key bands than the
+// rest (the ramp); pairing its two ends gives items of about one full band.
+// The host sets the counts from a model of the launch so that the last
+// round of workgroups holds the half-size items.
+template <typename T, bool SOFTCAP, bool FIXREF>
+__global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kPipe4Stages * kPipe4Tile];
+  // Every argument the first loads depend on, asked for at once, so that
+  // their loads leave in one batch and cost one round trip.
+  asm volatile("" : : "s"(a.kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
+               "s"(a.G), "s"(a.m), "s"(a.Lq), "s"(a.Lkv), "s"(a.causal), "s"(a.window), "s"(a.div_g.m),
+               "s"(a.div_g.s), "s"(a.div_items.m), "s"(a.div_items.s), "s"(a.div_hkv.m), "s"(a.div_hkv.s),
+               "s"(a.nwg), "s"(a.pf_items), "s"(a.pf_pairs), "s"(a.pf_ramp), "s"(a.pf_full));
+  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
+  // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
+  // range of (unit, item) pairs: the items of one unit then share their K/V
+  // tiles in one L2.
+  const int bid = blockIdx.x;
+  int lin = bid;
+  if ((a.nwg & 7) == 0) lin = (bid & 7) * (a.nwg >> 3) + (bid >> 3);
+  const int unit = fdiv(lin, a.div_items);
+  const int j = lin - unit * a.pf_items;
+  const int whole = a.pf_pairs + a.pf_full;
+  if (j >= whole) {
+    const int h = j - whole, half = a.m >> 1;
+    const int pblk = a.n_pos_blk - 1 - a.pf_full - (h >> 1);
+    pipe4_block<T, 1, SOFTCAP, FIXREF>(a, smem, unit, pblk * a.m + (h & 1) * half, half);
+    return;
+  }
+  int pb0 = a.n_pos_blk - 1 - (j - a.pf_pairs), pb1 = -1;
+  if (j < a.pf_pairs) {
+    pb0 = a.pf_ramp - 1 - j;
+    if (j < pb0) pb1 = j;
+  }
+  // At most two passes; one copy of the block code.
+  while (true) {
+    pipe4_block<T, 2, SOFTCAP, FIXREF>(a, smem, unit, pb0 * a.m, a.m);
+    if (pb1 < 0) break;
+    pb0 = pb1;
+    pb1 = -1;
+    __syncthreads();
   }
 }
 

@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_version_and_error_strings():
-    assert _lib.attn_version() == 102
+    assert _lib.attn_version() == 103
     for code in range(-11, 1):
         s = _lib.error_string(code)
         assert s and s != "unknown error code"
@@ -316,3 +316,79 @@ def test_noalloc_scratch_covers_every_plan():
     assert _lib.attn_fwd_noalloc(P, P, P, P, 1, 4, 3, 1, 64, 128, 1, 0, 0.0, 0, None) == _lib.MGQA_ERR_SHAPE
     assert _lib.attn_fwd_noalloc(P, P, P, ctypes.c_void_p(0x100008), 1, 4, 1, 1, 64, 128, 1, 0, 0.0, 0,
                                  None) == _lib.MGQA_ERR_ALIGN
+
+
+def _pipe_item_positions(info, B, Hq, Hkv, Lq):
+    """Query positions each work item of one unit covers, decoded from the
+    plan's item layout the way the head-size-128 prefill kernel decodes it."""
+    G = Hq // Hkv
+    m = info["rows_per_wg"] // G
+    n = -(-Lq // m)
+    items = info["workgroups"] // (B * Hkv)
+    assert items * B * Hkv == info["workgroups"]
+    pairs, ramp, full = info["pf_pairs"], info["pf_ramp"], info["pf_full"]
+    assert pairs == (ramp + 1) // 2 and full >= 0
+    halves = items - pairs - full
+    assert halves >= 0 and halves % 2 == 0
+    if halves:
+        assert m % 2 == 0
+    out = []
+    for j in range(items):
+        if j < pairs:
+            blocks = [ramp - 1 - j] + ([j] if j < ramp - 1 - j else [])
+            out.append([p for pb in blocks for p in range(pb * m, min(Lq, pb * m + m))])
+        elif j < pairs + full:
+            pb = n - 1 - (j - pairs)
+            out.append(list(range(pb * m, min(Lq, pb * m + m))))
+        else:
+            h = j - pairs - full
+            pb = n - 1 - full - (h >> 1)
+            q0 = pb * m + (h & 1) * (m // 2)
+            out.append(list(range(q0, min(Lq, q0 + m // 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 32, 4, 4096, 4096, 1, 1024),   # windowed causal: ramp halved
+    (2, 32, 4, 4096, 4096, 1, 0),      # causal
+    (2, 32, 4, 4096, 4096, 0, 0),      # no mask
+    (1, 64, 4, 4096, 4096, 1, 0),      # fewer units than XCDs: ramp paired
+    (1, 8, 1, 32768, 32768, 1, 0),     # one unit
+    (1, 16, 16, 4096, 4096, 1, 0),     # 128 positions per block
+    (2, 32, 4, 1000, 1000, 1, 0),      # partial last block
+    (2, 24, 8, 3001, 3001, 1, 700),    # G = 3: odd blocks of 42 positions
+    (2, 32, 4, 2048, 4096, 1, 1024),   # queries at the end of a longer key range
+    (4, 32, 8, 2048, 2048, 1, 512),
+    (3, 40, 5, 2500, 2500, 0, 300),    # bidirectional window
+])
+def test_prefill_items_cover_every_position_once(shape):
+    """The head-size-128 prefill plan splits each (batch row, kv head) into
+    work items -- ramp pairs, whole blocks, half blocks -- that together hold
+    every query position exactly once and no empty item."""
+    B, Hq, Hkv, Lq, Lkv, causal, window = shape
+    rc, info = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, 128, causal, window, 0.0)
+    assert rc == 0 and info["path"] == 0, info
+    items = _pipe_item_positions(info, B, Hq, Hkv, Lq)
+    assert all(items), "empty work item"
+    flat = sorted(p for it in items for p in it)
+    assert flat == list(range(Lq)), shape
+    # The same shape with another head size takes the generic prefill kernel
+    # with one whole block per workgroup and no item layout.
+    rc, other = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, 96, causal, window, 0.0)
+    assert rc == 0 and (other["pf_pairs"], other["pf_ramp"], other["pf_full"]) == (0, 0, 0)
+
+
+def test_prefill_item_layouts_chosen():
+    """Which layout the launch model picks for four prefill shapes: a causal
+    prefill with fewer units (batch rows x kv heads) than XCDs pairs the
+    ramp's ends, so every XCD gets an even share; a causal prefill of 128-
+    position blocks that fills one round halves every block; the windowed
+    causal prefill of 2 x 4 kv heads and an unmasked prefill keep one block
+    per workgroup, last first."""
+    rc, info = _lib.attn_plan(1, 64, 4, 4096, 4096, 128, 1, 0, 0.0)
+    assert info["pf_pairs"] > 0 and info["pf_ramp"] >= 2 * info["pf_pairs"] - 1
+    rc, info = _lib.attn_plan(1, 16, 16, 4096, 4096, 128, 1, 0, 0.0)
+    assert (info["pf_pairs"], info["pf_full"], info["workgroups"]) == (0, 0, 16 * 64)
+    for causal, window in ((1, 1024), (0, 0)):
+        rc, info = _lib.attn_plan(2, 32, 4, 4096, 4096, 128, causal, window, 50.0)
+        assert (info["pf_pairs"], info["pf_ramp"], info["pf_full"], info["workgroups"]) == (0, 0, 256, 8 * 256)

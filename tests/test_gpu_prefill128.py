@@ -14,6 +14,12 @@ Every case asserts that the plan takes the prefill path with head size 128
 and compares every output element with the float64 oracle (run head by head
 in a process pool for the larger shapes).
 
+ITEM_CASES reach each work-item layout of the kernel -- ramp blocks paired
+(with an odd ramp's middle block alone), half blocks of 64 rows (one 16-row
+block per wave) for every group size that allows them, a partial last block
+kept whole beside halved ones -- on the fixed-reference and running-maximum
+paths and with fp16; each asserts the layout it is meant to reach.
+
 The anti-aligned batches ("fixref_cap50_hot", "fixref_cap57p5_floor") push
 every visible score to the softcap's lower bound -c.  At c = 57.5, the largest
 softcap that keeps the fixed reference, the smallest probability is about
@@ -52,6 +58,19 @@ CASES = [
     ("nocap_g1_noncausal", 4, 16, 16, 520, 520, False, 0, 0.0, "bf16", 1.0, 310),
 ]
 
+# name, B, Hq, Hkv, Lq, Lkv, causal, window, softcap, dtype, q scale, seed, layout
+# layout: "pairs", "odd" (pairs and one middle block alone), "halves",
+# "all_halves", "mixed" (pairs, whole and half blocks)
+ITEM_CASES = [
+    ("items_odd_ramp_fixref", 2, 32, 4, 660, 700, True, 0, 50.0, "bf16", 8.0, 320, "odd"),
+    ("items_mixed_window_g2", 2, 32, 16, 1280, 1280, True, 256, 0.0, "bf16", 1.0, 321, "mixed"),
+    ("items_mixed_partial_last_g4", 2, 64, 16, 1003, 1003, True, 0, 30.0, "bf16", 6.0, 322, "mixed"),
+    ("items_halves_partial_last_g4", 1, 64, 16, 977, 977, True, 0, 0.0, "bf16", 1.0, 323, "halves"),
+    ("items_all_halves_g1_fixref", 2, 16, 16, 1280, 1280, True, 0, 30.0, "bf16", 6.0, 324, "all_halves"),
+    ("items_all_halves_g2_fp16", 2, 32, 16, 640, 640, True, 0, 20.0, "fp16", 4.0, 325, "all_halves"),
+    ("items_all_halves_g8_fixref", 2, 32, 4, 640, 640, True, 0, 50.0, "bf16", 8.0, 326, "all_halves"),
+]
+
 
 def _inputs(name, B, Hq, Hkv, Lq, Lkv, dtype, qscale, seed):
     q = synth.draw_array(seed, (B, Hq, Lq, 128), dtype)
@@ -74,6 +93,29 @@ def _inputs(name, B, Hq, Hkv, Lq, Lkv, dtype, qscale, seed):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_prefill128_parity(case, oracle_pool):
+    _check_case(case, oracle_pool)
+
+
+@pytest.mark.parametrize("case", ITEM_CASES, ids=lambda c: c[0])
+def test_prefill128_item_layouts(case, oracle_pool):
+    from masked_gqa_attention_amd import _lib
+    name, B, Hq, Hkv, Lq, Lkv, causal, window, softcap, dtype, qscale, seed, layout = case
+    rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, 128, int(causal), window, softcap,
+                              0 if dtype == "bf16" else 1)
+    assert rc == 0 and plan["path"] == 0, plan
+    items = plan["workgroups"] // (B * Hkv)
+    pairs, ramp, full = plan["pf_pairs"], plan["pf_ramp"], plan["pf_full"]
+    halves = items - pairs - full
+    got = {"pairs": pairs > 0 and halves == 0 and ramp % 2 == 0,
+           "odd": pairs > 0 and ramp % 2 == 1,
+           "halves": pairs == 0 and full > 0 and halves > 0,
+           "all_halves": pairs == 0 and full == 0 and halves > 0,
+           "mixed": pairs > 0 and full > 0 and halves > 0}[layout]
+    assert got, (layout, plan)
+    _check_case(case[:-1], oracle_pool)
+
+
+def _check_case(case, oracle_pool):
     from masked_gqa_attention_amd import _lib
     name, B, Hq, Hkv, Lq, Lkv, causal, window, softcap, dtype, qscale, seed = case
     rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, 128, int(causal), window, softcap,
