@@ -35,6 +35,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import re
 import os
 import subprocess
 import sys
@@ -336,12 +337,23 @@ def device_info(torch) -> dict:
             "compute_units": props.multi_processor_count,
             "max_sclk_mhz": (props.clock_rate / 1000.0) if getattr(props, "clock_rate", 0) else None,
             "sclk_now_mhz": None}
-    try:  # the current shader clock, from a child process (no GPU work of ours)
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+    # Shader clocks from rocm-smi in a child process (no GPU work of ours): the
+    # current one (the card is idle by then) and the highest supported level.
+    def smi_mhz(flag):
+        r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=20)
+        found = []
         for card in json.loads(r.stdout).values():
             for key, val in card.items():
-                if "sclk" in key.lower():
-                    info["sclk_now_mhz"] = float(str(val).strip("()Mhz "))
+                m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", str(val), re.I)
+                if "sclk" in key.lower() and m:
+                    found.append(float(m.group(1)))
+        return found
+    try:
+        now = smi_mhz("--showclocks")
+        info["sclk_now_mhz"] = now[0] if now else None
+        levels = smi_mhz("--showclkfrq")
+        if levels:
+            info["max_sclk_mhz"] = max(levels)
     except Exception:
         pass
     return info
