@@ -339,19 +339,22 @@ def device_info(torch) -> dict:
             "sclk_now_mhz": None}
     # Shader clocks from rocm-smi in a child process (no GPU work of ours): the
     # current one (the card is idle by then) and the highest supported level.
-    def smi_mhz(flag):
+    # --showclocks names its entries ("sclk clock speed:": "(2404Mhz)");
+    # --showclkfrq lists the shader clock levels by number ("2": "2400Mhz").
+    def smi_mhz(flag, want):
         r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=20)
+        out = r.stdout[r.stdout.index("{"):] if "{" in r.stdout else "{}"
         found = []
-        for card in json.loads(r.stdout).values():
+        for card in json.loads(out).values():
             for key, val in card.items():
                 m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", str(val), re.I)
-                if "sclk" in key.lower() and m:
+                if m and want(key):
                     found.append(float(m.group(1)))
         return found
     try:
-        now = smi_mhz("--showclocks")
+        now = smi_mhz("--showclocks", lambda key: "sclk" in key.lower())
         info["sclk_now_mhz"] = now[0] if now else None
-        levels = smi_mhz("--showclkfrq")
+        levels = smi_mhz("--showclkfrq", lambda key: key.strip().isdigit())
         if levels:
             info["max_sclk_mhz"] = max(levels)
     except Exception:

@@ -251,6 +251,26 @@ PipeSched pipe_schedule(long long units, int n, int m, int Lq, int Lkv, int caus
 
 }  // namespace
 
+// Largest number of 32-key steps in the key band of any block of m query
+// positions, or any number above `limit` once one block exceeds it.
+static int max_block_steps(int m, int Lq, int Lkv, int causal, int window, int limit) {
+  // A block's band spans at most m - 1 + window keys under a causal window,
+  // m - 1 + 2*window - 1 under a two-sided one, and Lkv keys in any case;
+  // 32-key steps over a span of n keys: at most (n + 30) / 32 + 1.
+  long long span = Lkv;
+  if (window > 0) span = std::min<long long>(span, (long long)m - 1 + (causal ? window : 2LL * window - 1));
+  if ((span + 30) / 32 + 1 <= limit) return (int)((span + 30) / 32 + 1);
+  int worst = 1;
+  for (int q0 = 0; q0 < Lq; q0 += m) {
+    int lo, hi;
+    block_band(q0, Lq - q0 < m ? Lq - q0 : m, Lq, Lkv, causal, window, &lo, &hi);
+    const int steps = hi / 32 - lo / 32 + 1;
+    if (steps > worst) worst = steps;
+    if (worst > limit) break;
+  }
+  return worst;
+}
+
 int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int window,
               float softcap, int dtype, Plan* plan) {
   const int err = validate(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype);
@@ -298,9 +318,19 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   p.path = kPathSplit;
   p.keys_per_tile = kSplitKeys;
   p.nwaves = kSplitWaves;
+  bool short_band = false;
   if (rows_all <= 16LL * max_nqb) {
     p.nqb = (int)((rows_all + 15) / 16);
     p.m = Lq;
+  } else if (d > 48 && d <= 96 && max_block_steps(16 * kEncNqb / G, Lq, Lkv, causal, window, kEncMaxSteps) <= kEncMaxSteps) {
+    // Short bands (at most kEncMaxSteps 32-key steps for a block of 48/G
+    // positions), head size 49..96: the short-band kernel, whatever the
+    // workgroup count.  Its eight waves split the band among themselves and
+    // merge in LDS; on the 729-token encoder with 1 to 8 heads this was
+    // faster than key splits across workgroups (4 heads: 8.5 against 10.6 us).
+    short_band = true;
+    p.nqb = kEncNqb;
+    p.m = 16 * kEncNqb / G;
   } else {
     p.nqb = 1;
     for (int nqb = max_nqb; nqb >= 1; --nqb) {
@@ -331,7 +361,7 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   long long ns = 1;
   int tps = 1 << 30;  // one split: the whole band
   int ncol = 1;
-  if (groups < kSplitTarget) {
+  if (groups < kSplitTarget && !short_band) {
     const int max_tiles = max_band_tiles(kSplitKeys);
     ns = (kSplitTarget + groups - 1) / groups;
     if (ns > max_tiles) ns = max_tiles;
@@ -361,10 +391,13 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
       ns = (max_tiles + tps - 1) / tps;
     }
   }
-  // Three 16-row blocks over an unsplit band of at most 768 keys, head size
-  // 49..96 (the 729-token encoder and shapes like it): the short-band kernel,
-  // eight waves that each take their own contiguous keys of the band.
-  if (p.nqb == kEncNqb && ns == 1 && d > 48 && d <= 96 && max_band_tiles(32) <= kEncMaxSteps) {
+  // The short-band kernel: eight waves that each take their own contiguous
+  // keys of a band of at most 768 keys (head size 49..96).  Chosen above for
+  // blocks of 48 rows; also taken by the rows of a multi-token step that fill
+  // three 16-row blocks when the band is left unsplit.
+  if (!short_band && p.nqb == kEncNqb && ns == 1 && d > 48 && d <= 96 && max_band_tiles(32) <= kEncMaxSteps)
+    short_band = true;
+  if (short_band) {
     p.path = kPathShort;
     p.nwaves = kEncWaves;
     p.keys_per_tile = 32 * kEncSteps;  // the most keys one wave takes

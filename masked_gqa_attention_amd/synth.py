@@ -118,17 +118,21 @@ WORKLOADS = {
 WORKLOAD_ORDER = list(WORKLOADS)
 
 # Shapes for the extensions beyond the five workloads: a multi-token decode
-# (4 new query positions per sequence, bottom-right causal), an encoder with
-# few heads (the key axis split across workgroups), and the long windowed
-# decode over a ring buffer of exactly the window's 4096 slots (ring start
-# 1234; the ring's Lkv is its slot count).
+# (4 new query positions per sequence, bottom-right causal), encoders with few
+# heads -- at 729 tokens (the short-band kernel: each workgroup's eight waves
+# split the key band among themselves) and at 1000 tokens (a band too long for
+# it: the key axis split across workgroups) -- and the long windowed decode
+# over a ring buffer of exactly the window's 4096 slots (ring start 1234; the
+# ring's Lkv is its slot count).
 NEXT_WORKLOADS = {
     w.name: w
     for w in [
         Workload("multitoken_decode_gqa4_Lq4_kv8192", B=8, Hq=32, Hkv=8, Lq=4, Lkv=8192, d=128,
                  causal=True, seed=5),
-        Workload("encoder_splitk_h4_L729_d72", B=1, Hq=4, Hkv=4, Lq=729, Lkv=729, d=72,
+        Workload("encoder_fewheads_h4_L729_d72", B=1, Hq=4, Hkv=4, Lq=729, Lkv=729, d=72,
                  causal=False, seed=6, dtype="fp16"),
+        Workload("encoder_splitk_h4_L1000_d72", B=1, Hq=4, Hkv=4, Lq=1000, Lkv=1000, d=72,
+                 causal=False, seed=8, dtype="fp16"),
         Workload("ring_decode_gqa16_S4096_w4096_cap30", B=4, Hq=64, Hkv=4, Lq=1, Lkv=4096, d=128,
                  causal=True, window=4096, softcap=30.0, sigma=0.5, seed=7),
     ]

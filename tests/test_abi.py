@@ -222,14 +222,22 @@ def test_workspace_layout_fits():
 
 
 def test_encoder_shapes_split_keys_when_row_blocks_are_few():
-    """Short non-causal sequences with few heads: the row blocks alone would
-    leave most compute units idle, so the plan splits the key axis too; with
-    16 heads the row blocks already fill the chip and there is no split."""
-    for H, want_split in ((1, True), (2, True), (4, True), (16, False)):
+    """Short non-causal sequences with few heads: with a band of at most 768
+    keys they run on the short-band kernel whatever the workgroup count (its
+    eight waves split the band); with a longer band, row blocks alone would
+    leave most compute units idle, so the plan splits the key axis across
+    workgroups; with 16 heads the row blocks already fill the chip."""
+    for H in (1, 2, 4, 8, 16):
         rc, info = _lib.attn_plan(1, H, H, 729, 729, 72, 0, 0, 0.0)
-        assert rc == 0 and info["path"] == (1 if want_split else 2), info
-        assert (info["nsplit"] > 1) == want_split, (H, info)
+        assert rc == 0 and info["path"] == 2 and info["nsplit"] == 1, (H, info)
+        assert info["workgroups"] == 16 * H and info["rows_per_wg"] == 48, (H, info)
+    for H in (1, 2, 4):
+        rc, info = _lib.attn_plan(1, H, H, 1000, 1000, 72, 0, 0, 0.0)
+        assert rc == 0 and info["path"] == 1 and info["nsplit"] > 1, (H, info)
         assert info["workgroups"] >= 256 or info["nsplit"] > 1, (H, info)
+    # A two-sided window short enough for the kernel keeps long sequences on it.
+    rc, info = _lib.attn_plan(2, 2, 2, 1100, 1100, 72, 0, 300, 0.0)
+    assert rc == 0 and info["path"] == 2, info
 
 
 def test_column_halves_plan():
@@ -264,7 +272,7 @@ def test_wide_split_plan():
     assert rc == 0 and info["keys_per_tile"] == 128, info
     rc, info = _lib.attn_plan(1, 16, 16, 729, 1500, 72, 1, 0, 0.0)     # 48-row blocks, long band
     assert rc == 0 and info["path"] == 1 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 48, info
-    rc, info = _lib.attn_plan(1, 16, 16, 700, 900, 80, 1, 300, 0.0)    # 32-row blocks
+    rc, info = _lib.attn_plan(1, 16, 16, 700, 900, 80, 1, 0, 0.0)      # 32-row blocks, long band
     assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 32, info
     rc, info = _lib.attn_plan(1, 48, 16, 729, 729, 40, 1, 0, 0.0)      # 64-row blocks
     assert rc == 0 and info["keys_per_tile"] == 128 and info["rows_per_wg"] == 64, info
@@ -273,8 +281,8 @@ def test_wide_split_plan():
 def test_short_band_plan():
     """Three 16-row blocks over an unsplit band of at most 768 keys and head
     sizes 49..96 take the short-band kernel (path 2, no workspace, 96 keys per
-    wave at most); longer bands, head size 48 or 128, and shapes with key
-    splits do not."""
+    wave at most), also with few heads; longer bands and head size 48 or 128
+    do not, and neither do decode rows that fit one split-KV workgroup."""
     def plan(*a):
         rc, info = _lib.attn_plan(*a)
         assert rc == 0, a
@@ -288,7 +296,8 @@ def test_short_band_plan():
     assert plan(1, 16, 16, 729, 729, 128, 0, 0, 0.0)["path"] == 1
     assert plan(1, 16, 16, 729, 768, 72, 1, 0, 0.0)["path"] == 2     # band of exactly 768 keys
     assert plan(1, 16, 16, 729, 769, 72, 1, 0, 0.0)["path"] == 1     # 769 keys: 25 steps
-    assert plan(1, 4, 4, 729, 729, 72, 0, 0, 0.0)["path"] == 1       # few heads: key splits
+    assert plan(1, 4, 4, 729, 729, 72, 0, 0, 0.0)["path"] == 2       # few heads: waves split the band
+    assert plan(8, 32, 8, 4, 700, 72, 1, 0, 0.0)["path"] == 1        # 16 rows per unit: split-KV
     assert plan(1, 16, 8, 800, 800, 80, 1, 300, 30.0)["path"] == 2   # two heads per kv head
     # ring buffers need the decode path
     P = ctypes.c_void_p(0x100000)

@@ -129,7 +129,7 @@ HOT_CASES = [
     ("hot_short_band_cap", 1, 16, 16, 729, 729, 72, False, 0, 30.0, "bf16", 12.0, 48, 96, 2),
     ("hot_short_band_190", 5, 16, 16, 190, 190, 72, False, 0, 0.0, "bf16", 12.0, 48, 96, 2),
     ("hot_3blocks_long_band", 1, 16, 16, 729, 1500, 72, True, 0, 0.0, "bf16", 12.0, 48, 128, 1),
-    ("hot_2blocks_window", 1, 16, 16, 700, 900, 80, True, 300, 0.0, "bf16", 12.0, 32, 128, 1),
+    ("hot_2blocks_long_band", 1, 16, 16, 700, 900, 80, True, 0, 0.0, "bf16", 12.0, 32, 128, 1),
     ("hot_4blocks_g3", 1, 48, 16, 729, 729, 40, True, 0, 0.0, "fp16", 5.0, 64, 128, 1),
 ]
 
