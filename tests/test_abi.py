@@ -401,3 +401,34 @@ def test_prefill_item_layouts_chosen():
     for causal, window in ((1, 1024), (0, 0)):
         rc, info = _lib.attn_plan(2, 32, 4, 4096, 4096, 128, causal, window, 50.0)
         assert (info["pf_pairs"], info["pf_ramp"], info["pf_full"], info["workgroups"]) == (0, 0, 256, 8 * 256)
+
+
+def test_gpu_sweep_reaches_every_plan_form():
+    """The seeded GPU sweep's shapes (fixed by its generator seeds) reach every
+    form the planner can pick, so the sweep checks each against the oracle."""
+    from .test_gpu_sweep import SHAPES
+    forms = set()
+    for i, B, Hq, Hkv, Lq, Lkv, d, causal, window, cap, dt in SHAPES:
+        rc, p = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), window, cap, 0 if dt == "bf16" else 1)
+        assert rc == 0
+        if p["path"] == 0 and d == 128:
+            items = p["workgroups"] // (B * Hkv)
+            forms.add("pipe_pairs" if p["pf_pairs"] else "pipe")
+            if items > p["pf_pairs"] + p["pf_full"]:
+                forms.add("pipe_halves")
+        elif p["path"] == 0:
+            forms.add("prefill")
+        elif p["path"] == 2:
+            forms.add("short_band")
+        else:
+            forms.add("split")
+            if p["nsplit"] > 1:
+                forms.add("key_splits")
+            if p["keys_per_tile"] == 256:
+                forms.add("wide")
+            if p["ncol"] == 2:
+                forms.add("column_halves")
+            forms.add(f"split_rows_{p['rows_per_wg']}")
+    want = {"pipe", "pipe_pairs", "pipe_halves", "prefill", "short_band", "split", "key_splits", "wide",
+            "column_halves", "split_rows_16", "split_rows_32", "split_rows_48"}
+    assert want <= forms, want - forms

@@ -1,6 +1,7 @@
 """Seeded random sweep of shapes through every plan the library can pick
-(pipelined and generic prefill, 4- and 8-wave split-KV with one to four row
-blocks, key splits, column halves): GQA ratios 1 to 16, head sizes that are
+(pipelined prefill with its work-item layouts, generic prefill, 4- and 8-wave
+split-KV with one to four row blocks, key splits, column halves, the
+short-band kernel): GQA ratios 1 to 16, head sizes that are
 multiples of 8 up to 128, ragged query and key lengths, bottom-right causal
 masks, one- and two-sided windows, softcaps, bf16 and fp16.  Every element is
 compared with the float64 oracle within the task page's tolerance, and two
@@ -82,6 +83,16 @@ def _targeted():
                     int(rng.choice([0, 150])), float(rng.choice([0.0, 30.0])), ["fp16", "bf16"][r]))
         out.append(("halves", 1, 16, 1, int(rng.integers(1, 3)), int(rng.integers(5000, 9000)), 128, True,
                     int(rng.integers(2000, 4000)), float(rng.choice([0.0, 30.0])), "bf16"))
+        # Head-size-128 prefill work items: causal ramp pairs, and half blocks.
+        L = int(rng.integers(262, 290))
+        out.append(("items_pairs", 2, 64, 8, L, L, 128, True, 0, float(rng.choice([0.0, 45.0])),
+                    ["bf16", "fp16"][r]))
+        L = int(rng.integers(340, 356))
+        out.append(("items_halves", 3, 32, 8, L, L, 128, False, 0, float(rng.choice([0.0, 20.0])),
+                    ["fp16", "bf16"][r]))
+        # Few heads over a short band: the short-band kernel with few workgroups.
+        out.append(("few_heads", 1, 2, 2, int(rng.integers(600, 729)), 729, 72, False,
+                    int(rng.choice([0, 200])), 0.0, ["fp16", "bf16"][r]))
     return [(N_CASES + i,) + t[1:] for i, t in enumerate(out)]
 
 
