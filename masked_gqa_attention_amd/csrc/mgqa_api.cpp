@@ -9,7 +9,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <functional>
 #include <mutex>
 #include <vector>
 
