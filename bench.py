@@ -37,6 +37,7 @@ import hashlib
 import json
 import re
 import os
+import shutil
 import subprocess
 import sys
 
@@ -53,6 +54,8 @@ LLC_BYTES = 256 * 1024 * 1024    # MI355X last-level (Infinity) cache
 COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate byte counters
 KERNEL_SRC = os.path.join(ROOT, "masked_gqa_attention_amd", "csrc", "mgqa_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_splitkv_kernel_decode_gqa4_kv8192.json")
+TRAFFIC_FILE_PREFILL = os.path.join(ROOT, "profiles",
+                                    "traffic_prefill_pipe4_kernel_prefill_gqa8_L4096_w1024_cap50.json")
 
 
 def log(msg):
@@ -341,8 +344,20 @@ def device_info(torch) -> dict:
     # current one (the card is idle by then) and the highest supported level.
     # --showclocks names its entries ("sclk clock speed:": "(2404Mhz)");
     # --showclkfrq lists the shader clock levels by number ("2": "2400Mhz").
+    def smi_cmd():
+        # rocm-smi is a Python script: run it with this interpreter, so that
+        # no process replaces itself through its "env python3" line.
+        path = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+        real = os.path.realpath(path)
+        try:
+            with open(real, "rb") as f:
+                is_python = b"python" in f.readline()
+        except OSError:
+            is_python = False
+        return [sys.executable, real] if is_python else [path]
+
     def smi_mhz(flag, want):
-        r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run(smi_cmd() + [flag, "--json"], capture_output=True, text=True, timeout=20)
         out = r.stdout[r.stdout.index("{"):] if "{" in r.stdout else "{}"
         found = []
         for card in json.loads(out).values():
@@ -362,13 +377,14 @@ def device_info(torch) -> dict:
     return info
 
 
-def load_traffic(steps_kernel_ms):
-    """Counter-derived HBM bytes per launch of the headline kernel, if the
-    counters were taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def load_traffic(path=TRAFFIC_FILE):
+    """Counter-derived HBM bytes per launch of a kernel (read + written, each
+    counter scaled by a known-size copy), if the counters were taken on the
+    current kernel source; otherwise None."""
+    if not os.path.exists(path):
         return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except Exception:
         return None
@@ -502,7 +518,7 @@ def main(argv=None) -> int:
     dev = device_info(torch)
     r, ms, steps, fig = headline
     w = r.w
-    traffic = load_traffic(ms)
+    traffic = load_traffic()
     line = {
         "metric": METRIC,
         "value": fig["value"],
@@ -528,7 +544,8 @@ def main(argv=None) -> int:
     if pre in results:
         rp = results[pre]
         line["roofline_prefill"] = {"bound": "mfma", "achieved": rp["value"], "peak": MFMA_PEAK_TFLOPS,
-                                    "unit": "TFLOP/s", "frac": rp["frac"], "traffic": None,
+                                    "unit": "TFLOP/s", "frac": rp["frac"],
+                                    "traffic": load_traffic(TRAFFIC_FILE_PREFILL),
                                     "kernel": rp["kernel"], "alg_flops_per_launch": rp["alg_flops"],
                                     "ms_per_launch": rp["ms"]}
     if pool is not None:
