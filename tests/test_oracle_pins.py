@@ -334,6 +334,30 @@ def _mut_no_max_subtraction(s, ok):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def _mut_causal_strict(pos, j, causal, window):
+    ok = _orig_visible(pos, j, False, window)
+    if causal:
+        ok &= j < pos
+    return ok
+
+
+def _mut_window_minus_one(pos, j, causal, window):
+    return _orig_visible(pos, j, causal, window - 1 if window > 1 else window)
+
+
+def _mut_softcap_unscaled_tanh(s, softcap):
+    return np.tanh(s) if softcap > 0 else s
+
+
+def _mut_one_sided_window_noncausal(pos, j, causal, window):
+    ok = np.ones(np.broadcast(pos, j).shape, dtype=bool)
+    if causal:
+        ok &= j <= pos
+    if window > 0:
+        ok &= (pos - j) < window
+    return ok
+
+
 _orig_visible = oa.visible
 
 MUTANTS = {
@@ -343,6 +367,10 @@ MUTANTS = {
     "heads_interleaved": [("kv_head", _mut_interleaved_heads)],
     "scale_one_over_d": [("scale", _mut_scale_one_over_d)],
     "unnormalised": [("softmax_masked", _mut_unnormalised)],
+    "causal_excludes_diagonal": [("visible", _mut_causal_strict)],
+    "window_minus_one": [("visible", _mut_window_minus_one)],
+    "softcap_tanh_unscaled": [("apply_softcap", _mut_softcap_unscaled_tanh)],
+    "window_one_sided_without_causal": [("visible", _mut_one_sided_window_noncausal)],
 }
 
 
