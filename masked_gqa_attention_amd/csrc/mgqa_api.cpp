@@ -284,16 +284,18 @@ int make_plan(int B, int Hq, int Hkv, int Lq, int Lkv, int d, int causal, int wi
   const int max_nqb = p.dv <= kSplitWideMaxDv ? kSplitMaxNqb : kSplitMaxNqbWide;
 
   // Prefill kernels: 256-row blocks (128-row blocks, two workgroups per CU,
-  // for head size 128), when that still gives a workgroup per CU.
+  // for head size 128; 128-row blocks of one 16-row block per wave for head
+  // sizes 104-120), when that still gives a workgroup per CU.
   const bool d128 = (d == 128);
-  const int rows_big = d128 ? 16 * kPipe4Waves * kPrefillNqb : 16 * kPrefillWaves * kPrefillNqb;
+  const int pf_nqb = (!d128 && p.dqk == 4) ? kPrefillNqbWide : kPrefillNqb;
+  const int rows_big = d128 ? 16 * kPipe4Waves * kPrefillNqb : 16 * kPrefillWaves * pf_nqb;
   const int m_big = rows_big / G;
   const long long wgs_big = units * ((Lq + m_big - 1) / m_big);
   if (rows_all > 16LL * max_nqb && wgs_big >= kCUs) {
     p.path = kPathPrefill;
     p.keys_per_tile = d128 ? kPipe4Keys : kPrefillKeys;
     p.nsplit = 1;
-    p.nqb = kPrefillNqb;
+    p.nqb = pf_nqb;
     p.nwaves = d128 ? kPipe4Waves : kPrefillWaves;
     p.rows_per_wg = 16 * p.nwaves * p.nqb;
     p.m = m_big;
@@ -524,7 +526,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 extern "C" {
 
-int attn_version(void) { return 103; }
+int attn_version(void) { return 104; }
 
 const char* attn_error_string(int code) {
   switch (code) {

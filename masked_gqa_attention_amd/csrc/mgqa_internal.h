@@ -12,6 +12,10 @@ namespace mgqa {
 constexpr int kPrefillKeys = 64;
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillNqb = 2;
+// Head sizes 104-120 (four 32-wide Q chunks, 128-wide P.V): one block of 16
+// rows per wave; with two, the accumulators and the staged next tile need
+// more than the 256 registers an 8-wave workgroup allows and spill.
+constexpr int kPrefillNqbWide = 1;
 // Head size 128: four waves x 2 blocks of 16 rows, 32-key tiles.
 constexpr int kPipe4Waves = 4;
 constexpr int kPipe4Keys = 32;

@@ -1916,7 +1916,12 @@ static hipError_t launch_typed(const Plan& plan, const KernelArgs& args, hipStre
     }
     hipLaunchKernelGGL((prefill_pipe4_kernel<T, SOFTCAP, false>), grid, dim3(64 * kPipe4Waves), 0, st, args);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, 2, 8, SOFTCAP>), grid, dim3(512), 0, st, args);
+    if constexpr (DQK == 4)  // head sizes 104-120: one 16-row block per wave
+      hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, kPrefillNqbWide, kPrefillWaves, SOFTCAP>), grid,
+                         dim3(64 * kPrefillWaves), 0, st, args);
+    else
+      hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, kPrefillNqb, kPrefillWaves, SOFTCAP>), grid,
+                         dim3(64 * kPrefillWaves), 0, st, args);
   }
   return hipGetLastError();
 }

@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_version_and_error_strings():
-    assert _lib.attn_version() == 103
+    assert _lib.attn_version() == 104
     for code in range(-11, 1):
         s = _lib.error_string(code)
         assert s and s != "unknown error code"
@@ -417,7 +417,7 @@ def test_gpu_sweep_reaches_every_plan_form():
             if items > p["pf_pairs"] + p["pf_full"]:
                 forms.add("pipe_halves")
         elif p["path"] == 0:
-            forms.add("prefill")
+            forms.add(f"prefill_rows_{p['rows_per_wg']}")
         elif p["path"] == 2:
             forms.add("short_band")
         else:
@@ -429,6 +429,6 @@ def test_gpu_sweep_reaches_every_plan_form():
             if p["ncol"] == 2:
                 forms.add("column_halves")
             forms.add(f"split_rows_{p['rows_per_wg']}")
-    want = {"pipe", "pipe_pairs", "pipe_halves", "prefill", "short_band", "split", "key_splits", "wide",
+    want = {"pipe", "pipe_pairs", "pipe_halves", "prefill_rows_256", "prefill_rows_128", "short_band", "split", "key_splits", "wide",
             "column_halves", "split_rows_16", "split_rows_32", "split_rows_48"}
     assert want <= forms, want - forms

@@ -26,6 +26,7 @@ CASES = [
     ("pipe4_running_max_fp16", 2, 32, 4, 512, 512, 128, True, 0, 0.0, "fp16", 4.0, (0, 128, 32, 1)),
     ("pipe4_half_blocks_fp16", 2, 32, 16, 640, 640, 128, True, 0, 20.0, "fp16", 4.0, (0, 128, 32, 1)),
     ("prefill_kernel_d64", 2, 32, 16, 1024, 1024, 64, True, 0, 30.0, "bf16", 6.0, (0, 256, 64, 1)),
+    ("prefill_kernel_d112_one_block", 2, 32, 16, 1024, 1024, 112, True, 0, 0.0, "fp16", 4.0, (0, 128, 64, 1)),
     ("short_band_d72", 1, 16, 16, 729, 729, 72, False, 0, 0.0, "fp16", 4.0, (2, 48, 96, 1)),
     ("split_4waves_nqb2", 1, 16, 16, 512, 512, 128, True, 100, 30.0, "bf16", 8.0, (1, 32, 128, 1)),
     ("split_wide_decode", 8, 32, 8, 1, 8192, 128, True, 0, 0.0, "bf16", 1.0, (1, 16, 256, 1)),

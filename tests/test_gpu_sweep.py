@@ -65,9 +65,10 @@ def _shapes():
 def _targeted():
     """Random lengths and options on shapes built to land on the plans a
     small random shape rarely reaches: the pipelined head-size-128 prefill,
-    the generic prefill, 8-wave split-KV with one and with three row blocks,
-    and column halves."""
+    the generic prefill (two and one 16-row blocks per wave), 8-wave split-KV
+    with one and with three row blocks, and column halves."""
     rng = np.random.default_rng(20261204)
+    rng_wide = np.random.default_rng(20261205)
     out = []
     for r in range(2):
         L = int(rng.integers(200, 400))
@@ -93,6 +94,11 @@ def _targeted():
         # Few heads over a short band: the short-band kernel with few workgroups.
         out.append(("few_heads", 1, 2, 2, int(rng.integers(600, 729)), 729, 72, False,
                     int(rng.choice([0, 200])), 0.0, ["fp16", "bf16"][r]))
+        # Generic prefill at head sizes 104-120 (one 16-row block per wave).
+        L = int(rng_wide.integers(520, 640))
+        out.append(("prefill_one_block", 2, 64, 16, L, L + int(rng_wide.integers(0, 40)),
+                    int(rng_wide.choice([104, 112, 120])), bool(1 - r), int(rng_wide.choice([0, 190])),
+                    float(rng_wide.choice([0.0, 35.0])), ["fp16", "bf16"][r]))
     return [(N_CASES + i,) + t[1:] for i, t in enumerate(out)]
 
 

@@ -37,9 +37,10 @@ def test_workload_parity(name, oracle_pool):
 
 
 # Shapes large enough (a workgroup per CU or more) that the plan picks the
-# prefill path -- the 8-wave, 256-row blocks for head sizes other than 128, and
-# for head size 128 the pipelined 4-wave, 128-row kernel that fills LDS with
-# direct global-to-LDS loads -- checked on every element.
+# prefill path -- the 8-wave, 256-row blocks for head sizes up to 96, 128-row
+# blocks (one 16-row block per wave) for head sizes 104-120, and for head size
+# 128 the pipelined 4-wave, 128-row kernel that fills LDS with direct
+# global-to-LDS loads -- checked on every element.
 LARGE_BLOCK_CASES = [
     # name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed
     ("lb_causal_window_cap_d128", 2, 32, 16, 2048, 2048, 128, True, 300, 20.0, "bf16", 201),
@@ -48,6 +49,8 @@ LARGE_BLOCK_CASES = [
     ("lb_fp16_d128", 2, 32, 16, 2048, 2048, 128, True, 0, 0.0, "fp16", 204),
     ("lb_causal_d64", 2, 32, 16, 2048, 2048, 64, True, 0, 0.0, "bf16", 205),
     ("lb_window_cap_d96_g8", 4, 64, 8, 1024, 1100, 96, True, 129, 30.0, "bf16", 206),
+    ("lb_causal_window_cap_d112", 2, 32, 16, 2048, 2048, 112, True, 500, 25.0, "bf16", 207),
+    ("lb_noncausal_fp16_d120_g4", 1, 32, 8, 1536, 1536, 120, False, 0, 0.0, "fp16", 208),
 ]
 
 
@@ -57,7 +60,7 @@ def test_large_block_parity(case, oracle_pool):
     name, B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype, seed = case
     rc, plan = _lib.attn_plan(B, Hq, Hkv, Lq, Lkv, d, int(causal), window, softcap,
                               0 if dtype == "bf16" else 1)
-    assert rc == 0 and plan["path"] == 0 and plan["rows_per_wg"] == (128 if d == 128 else 256), plan
+    assert rc == 0 and plan["path"] == 0 and plan["rows_per_wg"] == (128 if d > 96 else 256), plan
     announce(f"large block {name}")
     q = synth.draw_array(seed, (B, Hq, Lq, d), dtype)
     k = synth.draw_array(seed + 1, (B, Hkv, Lkv, d), dtype)
