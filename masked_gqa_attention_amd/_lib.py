@@ -13,6 +13,10 @@ import os
 import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmgqa.so")
+# The measurement build: the same entry points plus the timeline calls of
+# include/mgqa_timeline.h.  Chosen with use_timeline_build() before the first
+# call of a process.
+TIMELINE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmgqa_timeline.so")
 
 # Error codes (include/mgqa.h)
 MGQA_OK = 0
@@ -36,6 +40,9 @@ MGQA_F32 = 2
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_noalloc", "attn_fwd_cache", "attn_fwd_cache_append",
            "kv_cache_append", "attn_workspace_bytes", "attn_plan", "attn_error_string", "attn_version")
 
+# Extra symbols of the timeline build (include/mgqa_timeline.h).
+TIMELINE_EXPORTS = ("attn_timeline_layout", "attn_timeline_clear", "attn_timeline_read")
+
 MGQA_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _lib = None
@@ -45,8 +52,17 @@ class LibraryMissing(RuntimeError):
     pass
 
 
+def use_timeline_build() -> None:
+    """Make this process use libmgqa_timeline.so instead of libmgqa.so.  Only
+    before the library is opened: one process uses one build."""
+    global LIB_PATH
+    if _lib is not None and LIB_PATH != TIMELINE_LIB_PATH:
+        raise RuntimeError("libmgqa.so is already open in this process")
+    LIB_PATH = TIMELINE_LIB_PATH
+
+
 def load() -> ctypes.CDLL:
-    """Open libmgqa.so (once) and declare the signatures."""
+    """Open the library (once) and declare the signatures."""
     global _lib
     if _lib is not None:
         return _lib
@@ -76,6 +92,13 @@ def load() -> ctypes.CDLL:
     lib.attn_error_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
     lib.attn_version.restype = i
+    if LIB_PATH == TIMELINE_LIB_PATH:
+        lib.attn_timeline_layout.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.attn_timeline_layout.restype = i
+        lib.attn_timeline_clear.argtypes = [vp]
+        lib.attn_timeline_clear.restype = i
+        lib.attn_timeline_read.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), sz]
+        lib.attn_timeline_read.restype = i
     _lib = lib
     return lib
 
@@ -142,3 +165,20 @@ def attn_plan(B, Hq, Hkv, Lq, Lkv, d, causal, window, softcap, dtype=MGQA_BF16):
 
 def attn_version() -> int:
     return int(load().attn_version())
+
+
+def attn_timeline_layout():
+    """(events per record, records) of the timeline build."""
+    ev, mw = ctypes.c_int(), ctypes.c_int()
+    rc = load().attn_timeline_layout(ctypes.byref(ev), ctypes.byref(mw))
+    if rc != 0:
+        raise RuntimeError(f"attn_timeline_layout: {error_string(rc)}")
+    return ev.value, mw.value
+
+
+def attn_timeline_clear(stream) -> int:
+    return int(load().attn_timeline_clear(stream))
+
+
+def attn_timeline_read(host_ptr, words) -> int:
+    return int(load().attn_timeline_read(ctypes.cast(host_ptr, ctypes.POINTER(ctypes.c_ulonglong)), words))

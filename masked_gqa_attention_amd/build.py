@@ -1,11 +1,14 @@
-"""Build the gfx950 shared library libmgqa.so in-tree with hipcc.
+"""Build the gfx950 shared libraries in-tree with hipcc.
 
     python -m masked_gqa_attention_amd.build [--verbose]
 
 Every HIP source is compiled for gfx950 only, with packed fp32 instructions
 disabled and matrix-core accumulators in architectural registers, and
 linked into masked_gqa_attention_amd/libmgqa.so next to this file.  The
-build always recompiles (it is the "does it build" check).
+same sources with the kernels compiled under MGQA_TIMELINE give
+libmgqa_timeline.so, the measurement build with per-wave timestamps
+(include/mgqa_timeline.h).  The build always recompiles (it is the "does it
+build" check).
 """
 from __future__ import annotations
 
@@ -21,9 +24,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmgqa.so")
+OUT_TIMELINE = os.path.join(PKG, "libmgqa_timeline.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["mgqa_api.cpp", "mgqa_kernels.hip", "mgqa_cache.hip"]
+TIMELINE_SOURCE = "mgqa_kernels.hip"  # the only source with timeline marks
 
 ARCH = "gfx950"
 COMMON = [
@@ -46,9 +51,10 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, timeline: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".timeline.o" if timeline else ".o"))
+    defs = ["-DMGQA_TIMELINE"] if timeline else []
+    cmd = [hipcc(), *COMMON, *defs, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,18 +67,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libmgqa.so and libmgqa_timeline.so; returns the former's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(TIMELINE_SOURCE, True)]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    plain = objs[:len(SOURCES)]
+    timeline = [objs[-1] if s == TIMELINE_SOURCE else o for s, o in zip(SOURCES, plain)]
+    _link(plain, OUT, verbose)
+    _link(timeline, OUT_TIMELINE, verbose)
     return OUT
 
 

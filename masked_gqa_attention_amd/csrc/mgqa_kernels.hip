@@ -39,6 +39,10 @@
 #include <type_traits>
 
 #include "mgqa_internal.h"
+#ifdef MGQA_TIMELINE
+#include "mgqa.h"
+#include "mgqa_timeline.h"
+#endif
 
 namespace mgqa {
 
@@ -56,6 +60,69 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_inff();
 // Lazy rescale threshold in base-2 exponent units.
 constexpr float kRescaleSlack = 8.0f;
+
+// ---------------------------------------------------------------------------
+// Timeline build (compiled with MGQA_TIMELINE defined; in the library proper
+// every Timeline call below is an empty inline function and generates no
+// code).  At each event of its kernel a wave reads the 100 MHz real-time
+// counter, between scheduling barriers so that the compiler moves no work
+// across the mark, and keeps it in one lane of a single vector register
+// (lanes 0-7: low words of events 0-7, lanes 8-15: high words, lane 16: the
+// record slot), so that a mark holds no scalar registers and issues no
+// memory operation.  When the wave ends, lanes 0-17 write the record.  Record
+// layout and the events of each kernel: include/mgqa_timeline.h.
+// ---------------------------------------------------------------------------
+#ifdef MGQA_TIMELINE
+constexpr int kTlEvents = MGQA_TIMELINE_EVENTS;
+constexpr int kTlMaxWaves = MGQA_TIMELINE_MAX_WAVES;
+static_assert(kTlEvents == 8, "lanes 0-15 hold the event times");
+__device__ __attribute__((aligned(256))) unsigned long long g_timeline[(size_t)kTlMaxWaves * (kTlEvents + 1)];
+
+struct Timeline {
+  unsigned v;
+  // Lane LANE of v = x (x wave-uniform).
+  template <int LANE>
+  __device__ __forceinline__ void put(unsigned x) {
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"(LANE));
+  }
+  __device__ __forceinline__ explicit Timeline(int waves) {
+    v = 0u;
+    put<16>(__builtin_amdgcn_readfirstlane(blockIdx.x * (unsigned)waves + (threadIdx.x >> 6)));
+  }
+  template <int EV>
+  __device__ __forceinline__ void mark() {
+    static_assert(EV >= 0 && EV < kTlEvents, "event index");
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+    put<EV>((unsigned)t);
+    put<8 + EV>((unsigned)(t >> 32));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Word 0 = 1 | XCD << 4 | HW_ID << 32; events not reached read 0.
+  __device__ __forceinline__ void flush() {
+    const unsigned slot = __builtin_amdgcn_readlane(v, 16);
+    if (slot >= (unsigned)kTlMaxWaves) return;
+    unsigned xcc, hw;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    unsigned* rec = reinterpret_cast<unsigned*>(g_timeline + (size_t)slot * (kTlEvents + 1));
+    const int lane = threadIdx.x & 63;
+    if (lane < 16)
+      rec[2 + 2 * (lane & 7) + (lane >> 3)] = v;
+    else if (lane == 16)
+      rec[0] = 1u | ((xcc & 0xFu) << 4);
+    else if (lane == 17)
+      rec[1] = hw;
+  }
+};
+#else
+struct Timeline {
+  __device__ __forceinline__ explicit Timeline(int) {}
+  template <int EV>
+  __device__ __forceinline__ void mark() {}
+  __device__ __forceinline__ void flush() {}
+};
+#endif
 
 // ---------------------------------------------------------------------------
 // Element-type traits: the MFMA and the float -> storage conversion.
@@ -545,6 +612,8 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
+  Timeline tl(NWAVES);
+  tl.mark<0>();
 
   // Every argument the first loads depend on, asked for at once, so that
   // their loads leave in one batch and cost one round trip.
@@ -611,6 +680,7 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   kt.store(smem, tid);
   vt.store(smem + KEYS * KP, tid);
   __syncthreads();
+  tl.mark<1>();
   for (int t = t_begin; t < t_end; ++t) {
     const int k0 = t * KEYS;
     const int cur = (t - t_begin) & 1;
@@ -636,10 +706,13 @@ __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
     }
     __syncthreads();
   }
+  tl.mark<2>();
 
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb)
     if (rok[qb]) store_row<T, DV>(og + roff[qb], o[qb], 1.0f / ls[qb][0], d, g4);
+  tl.mark<7>();
+  tl.flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -865,7 +938,8 @@ __device__ __forceinline__ void pipe_step(bool mask, const uint16_t* Kst, const 
 // stages the first block's last steps read.
 // ---------------------------------------------------------------------------
 template <typename T, int NQB, bool SOFTCAP, bool FIXREF>
-__device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem, int unit, int q0, int m_item) {
+__device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem, int unit, int q0, int m_item,
+                                            Timeline& tl, bool second) {
   constexpr int NWAVES = 4, D = 128, KEYS = 32, TILE = kPipe4Tile, NS = kPipe4Stages;
   constexpr int IPW = KEYS / 4 / NWAVES;  // 4-row direct-to-LDS loads per wave per tensor
   static_assert(IPW == 2, "the wait counts below assume two loads per tensor per wave");
@@ -969,6 +1043,8 @@ __device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem,
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
+  if (second) tl.mark<4>();
+  else tl.mark<1>();
 
   float m_e[NQB];
   f32x4 o[NQB][8], ls[NQB];
@@ -1058,6 +1134,8 @@ __device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem,
     step(S4{}, t, sb, sa, pa, pb);
     if (++t >= t_end) { last = 9; break; }
   }
+  if (second) tl.mark<5>();
+  else tl.mark<2>();
   // P.V and row sums of the last tile (its probabilities are in pa after an
   // even-numbered step of the turn, in pb after an odd one).
   {
@@ -1089,6 +1167,8 @@ __device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem,
       store_row<T, 8>(og + ro, o[qb], 1.0f / ls[qb][0], D, g4);
     }
   }
+  if (second) tl.mark<6>();
+  else tl.mark<3>();
 }
 
 // Work items of one unit, in launch order (item j; n = n_pos_blk blocks of m
@@ -1105,6 +1185,8 @@ __device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem,
 template <typename T, bool SOFTCAP, bool FIXREF>
 __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kPipe4Stages * kPipe4Tile];
+  Timeline tl(kPipe4Waves);
+  tl.mark<0>();
   // Every argument the first loads depend on, asked for at once, so that
   // their loads leave in one batch and cost one round trip.
   asm volatile("" : : "s"(a.kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
@@ -1124,7 +1206,9 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
   if (j >= whole) {
     const int h = j - whole, half = a.m >> 1;
     const int pblk = a.n_pos_blk - 1 - a.pf_full - (h >> 1);
-    pipe4_block<T, 1, SOFTCAP, FIXREF>(a, smem, unit, pblk * a.m + (h & 1) * half, half);
+    pipe4_block<T, 1, SOFTCAP, FIXREF>(a, smem, unit, pblk * a.m + (h & 1) * half, half, tl, false);
+    tl.mark<7>();
+    tl.flush();
     return;
   }
   int pb0 = a.n_pos_blk - 1 - (j - a.pf_pairs), pb1 = -1;
@@ -1133,13 +1217,17 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
     if (j < pb0) pb1 = j;
   }
   // At most two passes; one copy of the block code.
+  bool second = false;
   while (true) {
-    pipe4_block<T, 2, SOFTCAP, FIXREF>(a, smem, unit, pb0 * a.m, a.m);
+    pipe4_block<T, 2, SOFTCAP, FIXREF>(a, smem, unit, pb0 * a.m, a.m, tl, second);
     if (pb1 < 0) break;
     pb0 = pb1;
     pb1 = -1;
+    second = true;
     __syncthreads();
   }
+  tl.mark<7>();
+  tl.flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -1182,6 +1270,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g4 = lane >> 4;
+  Timeline tl(NW);
+  tl.mark<0>();
   // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8),
   // each XCD with its own L2.  Renumber so that every XCD gets a contiguous
   // range of (group, split) pairs: the position blocks of one unit, which
@@ -1299,6 +1389,7 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     qpos[qb] = q0 + pl + off;
     load_q<DQK>(qf[qb], qg + roff, rok, d, g4);
   }
+  tl.mark<1>();
 
   float m_e[NQB];
   f32x4 ls[NQB], o[NQB][DV];
@@ -1343,6 +1434,7 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       vt.store(Vs, tid);
       if (it + 2 < ntile) fetch_into(kt, vt, false, tile_at(it + 2) * KEYS);
       __syncthreads();
+      if (it == 0) tl.mark<2>();
       compute(tile_at(it) * KEYS);
       if (it + 1 >= ntile) break;
       __syncthreads();
@@ -1367,6 +1459,7 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       vt.store(Vs, tid);
       if (more) fetch_v(kn);
       __syncthreads();
+      if (it == 0) tl.mark<2>();
       const int w0 = k0 + 32 * wave;
       if (w0 > key_hi || w0 + 31 < key_lo) continue;
       bool full = w0 + 32 <= a.Lkv;
@@ -1386,6 +1479,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
                                                           g4);
     }
   }
+
+  tl.mark<3>();
 
   // ---- merge the wave states (fixed order) ------------------------------------
   // Every wave writes its (max, sum, unnormalised rows) of all row blocks to
@@ -1449,10 +1544,15 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
       if (c4 == 0) st_dev8(rs_ml, (pml + r) * 8, f32x2{M, L});
     }
   }
-  if (a.nsplit == 1) return;
+  tl.mark<4>();
+  if (a.nsplit == 1) {
+    tl.flush();
+    return;
+  }
 
   wait_vmem_done();
   __syncthreads();
+  tl.mark<5>();
   if (tid == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(a.ws_cnt + grp * NCOL + half, 1u, __ATOMIC_RELAXED,
@@ -1460,7 +1560,11 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     last_flag = (prev == (unsigned)(a.nsplit - 1)) ? 1 : 0;
   }
   __syncthreads();
-  if (!last_flag) return;
+  tl.mark<6>();
+  if (!last_flag) {
+    tl.flush();
+    return;
+  }
 
   // ---- last arrival: merge all splits in split order ---------------------------------
   // Online merge over groups of CHUNK splits (4, 8 or 16: the smallest that
@@ -1524,6 +1628,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
     merge_splits(std::integral_constant<int, 16>{});
   if (tid == 0)
     __hip_atomic_store(a.ws_cnt + grp * NCOL + half, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  tl.mark<7>();
+  tl.flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -1571,6 +1677,8 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
+  Timeline tl(kEncWaves);
+  tl.mark<0>();
   // Every argument the first loads depend on, asked for at once.
   const long long kv_stride = a.kv_stride;
   asm volatile("" : : "s"(kv_stride), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.n_pos_blk), "s"(a.Hkv), "s"(a.Hq),
@@ -1686,6 +1794,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
               rs_v, (__attribute__((address_space(3))) void*)(myv + st * 32 * VPITCH + i * 512), 16, (int)voff[i],
               (int)(st * step_bytes), 0, 0);
   }
+  tl.mark<1>();
 
   // ---- scores S^T = K Q^T of every step ------------------------------------
   // Straight-line over all NS steps; steps past this wave's share are masked
@@ -1702,6 +1811,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
         for (int t = 0; t < DQK; ++t) acc = Elem<T>::mfma(kf[st][hh][t], qf[qb][t], acc);
         s[st][hh][qb] = acc;
       }
+  tl.mark<2>();
 
   // ---- mask: steps crossing a band edge or the end of the keys, and steps
   // past this wave's share (all keys) ------------------------------------------
@@ -1787,6 +1897,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
       ls[qb] = Elem<T>::mfma(ones, pk[st][qb], ls[qb]);
     }
   }
+  tl.mark<3>();
 
   // ---- O^T = V^T P^T over the range ------------------------------------------
   // Transposed reads as in the other kernels: lane s of a 16-lane group points
@@ -1808,6 +1919,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
       for (int qb = 0; qb < NQB; ++qb) o[qb][db] = Elem<T>::mfma(vf, pk[st][qb], o[qb][db]);
     }
   }
+  tl.mark<4>();
 
   // ---- merge the eight wave states in wave order -----------------------------
   // The products above consumed this wave's V reads, so its region is free.
@@ -1823,6 +1935,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
       *reinterpret_cast<f32x4*>(&wo[(16 * qb + c16) * OPITCH + 16 * db + 4 * g4]) = o[qb][db];
   }
   __syncthreads();
+  tl.mark<5>();
   // Weight of wave w's row r: 2^(m_w - M) / L with M the row's maximum over
   // the waves and L = sum_w 2^(m_w - M) l_w (each sum in wave order); one
   // thread per (row, wave).
@@ -1838,6 +1951,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     wf[w][r] = (wm[w][r] == kNegInf) ? 0.f : fast_exp2(wm[w][r] - M) / L;
   }
   __syncthreads();
+  tl.mark<6>();
   constexpr int C4 = DV * 4;  // float4 chunks of one output row
   constexpr int JN = (NQB * 16 * C4 + 64 * NW - 1) / (64 * NW);
 #pragma unroll
@@ -1854,6 +1968,8 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
     const size_t oo = (((size_t)b * a.Hq + kvh * G + (r - pr * G)) * a.Lq + q0 + pr) * d + 4 * c4;
     *reinterpret_cast<u32x2*>(og + oo) = u32x2{Elem<T>::pack2(acc[0], acc[1]), Elem<T>::pack2(acc[2], acc[3])};
   }
+  tl.mark<7>();
+  tl.flush();
 }
 
 __global__ void zero_kernel(uint32_t* p, size_t n) {
@@ -1969,3 +2085,38 @@ int launch_zero(void* p, size_t words, void* stream) {
 }
 
 }  // namespace mgqa
+
+#ifdef MGQA_TIMELINE
+// Timeline build only: the wave records (include/mgqa_timeline.h).
+static int timeline_address(void** ptr) {
+  *ptr = nullptr;
+  if (hipGetSymbolAddress(ptr, HIP_SYMBOL(mgqa::g_timeline)) != hipSuccess || *ptr == nullptr) return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+
+extern "C" int attn_timeline_layout(int* events, int* max_waves) {
+  if (events == nullptr || max_waves == nullptr) return MGQA_ERR_NULL;
+  *events = mgqa::kTlEvents;
+  *max_waves = mgqa::kTlMaxWaves;
+  return MGQA_OK;
+}
+
+extern "C" int attn_timeline_clear(void* stream) {
+  void* ptr;
+  const int err = timeline_address(&ptr);
+  if (err != MGQA_OK) return err;
+  const size_t words32 = sizeof(mgqa::g_timeline) / 4;
+  return mgqa::launch_zero(ptr, words32, stream) == hipSuccess ? MGQA_OK : MGQA_ERR_HIP;
+}
+
+extern "C" int attn_timeline_read(unsigned long long* host, size_t words) {
+  if (host == nullptr) return MGQA_ERR_NULL;
+  if (words > sizeof(mgqa::g_timeline) / 8) return MGQA_ERR_RANGE;
+  void* ptr;
+  const int err = timeline_address(&ptr);
+  if (err != MGQA_OK) return err;
+  if (hipDeviceSynchronize() != hipSuccess) return MGQA_ERR_HIP;
+  if (words > 0 && hipMemcpy(host, ptr, words * 8, hipMemcpyDeviceToHost) != hipSuccess) return MGQA_ERR_HIP;
+  return MGQA_OK;
+}
+#endif

@@ -18,8 +18,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libmgqa.so not built (python -m masked_gqa_attention_amd.build)")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)))
 
@@ -36,6 +36,38 @@ def test_library_exports_every_header_symbol():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in header_functions():
         assert name in exported, name
+
+
+def _exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+@pytest.mark.skipif(not os.path.exists(_lib.TIMELINE_LIB_PATH), reason="libmgqa_timeline.so not built")
+def test_timeline_build_exports():
+    """The measurement build exports every entry point of both headers; the
+    library proper has none of the timeline calls."""
+    tl_header = os.path.join(ROOT, "include", "mgqa_timeline.h")
+    assert header_functions(tl_header) == sorted(_lib.TIMELINE_EXPORTS)
+    tl = _exported(_lib.TIMELINE_LIB_PATH)
+    for name in header_functions() + header_functions(tl_header):
+        assert name in tl, name
+    plain = _exported(_lib.LIB_PATH)
+    assert not plain & set(_lib.TIMELINE_EXPORTS)
+
+
+@pytest.mark.skipif(not os.path.exists(_lib.TIMELINE_LIB_PATH), reason="libmgqa_timeline.so not built")
+def test_timeline_calls_validate_before_hip():
+    """Layout, and the argument checks of the read call, need no GPU."""
+    tl = ctypes.CDLL(_lib.TIMELINE_LIB_PATH)
+    ev, mw = ctypes.c_int(), ctypes.c_int()
+    assert tl.attn_timeline_layout(ctypes.byref(ev), ctypes.byref(mw)) == 0
+    assert (ev.value, mw.value) == (8, 1 << 16)
+    assert tl.attn_timeline_layout(None, ctypes.byref(mw)) == _lib.MGQA_ERR_NULL
+    tl.attn_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    assert tl.attn_timeline_read(None, 1) == _lib.MGQA_ERR_NULL
+    buf = (ctypes.c_ulonglong * 1)()
+    assert tl.attn_timeline_read(buf, (1 << 16) * 9 + 1) == _lib.MGQA_ERR_RANGE
 
 
 def test_version_and_error_strings():
