@@ -763,14 +763,19 @@ struct PipeAddr {
 // block), fp32.
 template <bool SOFTCAP, int I0 = 0, int N = 4>
 __device__ __forceinline__ void pipe_probs(const f32x4& x, float mref, const KernelArgs& a, float (&p)[4]) {
+  if (SOFTCAP) {
+    // Stage by stage over the N scores, so that N independent chains of
+    // dependent transcendentals are in flight instead of one.
+    float t[4];
 #pragma unroll
-  for (int i = I0; i < I0 + N; ++i) {
-    if (SOFTCAP) {
-      const float r = fast_rcp(fast_exp2(x[i] * a.gamma) + 1.0f);
-      p[i] = fast_exp2(__builtin_fmaf(r, -2.0f * a.c2, a.c2 - mref));
-    } else {
-      p[i] = fast_exp2(__builtin_fmaf(x[i], a.alpha, -mref));
-    }
+    for (int i = I0; i < I0 + N; ++i) t[i] = fast_exp2(x[i] * a.gamma);
+#pragma unroll
+    for (int i = I0; i < I0 + N; ++i) t[i] = fast_rcp(t[i] + 1.0f);
+#pragma unroll
+    for (int i = I0; i < I0 + N; ++i) p[i] = fast_exp2(__builtin_fmaf(t[i], -2.0f * a.c2, a.c2 - mref));
+  } else {
+#pragma unroll
+    for (int i = I0; i < I0 + N; ++i) p[i] = fast_exp2(__builtin_fmaf(x[i], a.alpha, -mref));
   }
 }
 
@@ -1070,14 +1075,14 @@ __device__ __forceinline__ void pipe4_block(const KernelArgs& a, uint16_t* smem,
       sa[qb][hh] = acc;
     }
 
+  // Integer flags and an explicit wave-uniform result keep the test in
+  // scalar registers (as booleans it was built as a lane mask in vector
+  // registers on every step).
   auto step_full = [&](int kg0) {
-    bool full = kg0 + KEYS <= a.Lkv;
-    if (a.causal) full = full && (kg0 + KEYS - 1 <= pos_min);
-    if (a.window > 0) {
-      full = full && (pos_max - kg0 < a.window);
-      if (!a.causal) full = full && (kg0 + KEYS - 1 - pos_min < a.window);
-    }
-    return full;
+    int full = kg0 + KEYS <= a.Lkv;
+    full &= (a.causal == 0) | (kg0 + KEYS - 1 <= pos_min);
+    full &= (a.window <= 0) | ((pos_max - kg0 < a.window) & ((a.causal != 0) | (kg0 + KEYS - 1 - pos_min < a.window)));
+    return __builtin_amdgcn_readfirstlane(full) != 0;
   };
   // Step t (tile t in stage ST, compile time): softmax of tile t, scores of
   // tile t+1 (stage ST+1; discarded after the last tile), P.V of tile t-1
