@@ -28,6 +28,11 @@ least 1 ms of back-to-back calls ("spread": median, 10th and 90th percentile
 of the per-call time over the rounds).  Inputs
 rotate over several copies so that repeated calls stream from HBM rather than
 from the 256 MB last-level cache.  Prints ONE JSON line.
+Besides "roofline" (the headline decode against HBM) the line carries
+"roofline_prefill" (the windowed softcapped prefill against the bf16 MFMA
+peak) and "roofline_prefill_trans" (the same launches against the
+transcendental unit: three transcendental instructions per in-band pair with
+the softcap, one without, over a peak of a quarter of the fp32 lane rate).
 """
 from __future__ import annotations
 
@@ -50,6 +55,18 @@ HEADLINE = "decode_gqa4_kv8192"
 METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 MFMA
+# Transcendental instructions (v_exp_f32, v_rcp_f32): a quarter of the fp32
+# vector lane rate, i.e. 8 lanes per clock per SIMD: 256 CUs x 4 SIMDs x 8 x
+# 2.4 GHz, in tera-operations per second.
+TRANS_PEAK_TOPS = 256 * 4 * 8 * 2.4e9 / 1e12
+
+
+def trans_ops_per_pair(softcap: float) -> int:
+    """Transcendental instructions the method needs per in-band (query, key)
+    pair on this chip, which has no tanh instruction: the softmax exponential,
+    plus for the softcap c*tanh(s/c) = c - 2c/(exp(2s/c) + 1) one exponential
+    and one reciprocal."""
+    return 3 if softcap > 0 else 1
 LLC_BYTES = 256 * 1024 * 1024    # MI355X last-level (Infinity) cache
 COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate byte counters
 KERNEL_SRC = os.path.join(ROOT, "masked_gqa_attention_amd", "csrc", "mgqa_kernels.hip")
@@ -548,6 +565,14 @@ def main(argv=None) -> int:
                                     "traffic": load_traffic(TRAFFIC_FILE_PREFILL),
                                     "kernel": rp["kernel"], "alg_flops_per_launch": rp["alg_flops"],
                                     "ms_per_launch": rp["ms"]}
+        # Secondary roofline of the same launches: the transcendental unit.
+        wp = synth.WORKLOADS[pre]
+        ops = rp["alg_flops"] / (4 * wp.d) * trans_ops_per_pair(wp.softcap)
+        tops = ops / (rp["ms"] * 1e-3) / 1e12
+        line["roofline_prefill_trans"] = {"bound": "alu", "achieved": tops, "peak": TRANS_PEAK_TOPS,
+                                          "unit": "Tops/s", "frac": tops / TRANS_PEAK_TOPS, "traffic": None,
+                                          "kernel": rp["kernel"], "alg_ops_per_launch": ops,
+                                          "ops_per_pair": trans_ops_per_pair(wp.softcap)}
     if pool is not None:
         log("oracle legs (every workload, whole input, process pool) ...")
         for name, (wk, host, gpu_out) in kept.items():
