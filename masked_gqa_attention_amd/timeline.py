@@ -18,8 +18,9 @@ no arithmetic; the GPU tests check it) but its register allocation differs a
 little, so its durations are close to, not equal to, the library's.
 
 --check fails (exit status 1) unless every wave of every launch left a
-record with non-decreasing event times; --save-output writes the first
-copy's output of the last launch (numpy, storage dtype) for a bit comparison.
+record with non-decreasing event times; --save-output writes the output of
+one more call on the first input copy (the seeded inputs; numpy, storage
+dtype) for a bit comparison.
 """
 from __future__ import annotations
 
@@ -168,11 +169,14 @@ def summarise(rec: np.ndarray, kernel: str) -> dict:
 def markdown(w: synth.Workload, kernel: str, plan: dict, waves_per_wg: int, runs: list) -> str:
     lines = [f"Workload `{w.name}` ({w.describe()}), kernel `{kernel}`, {plan['workgroups']} workgroups of "
              f"{waves_per_wg} waves; times in µs from the first wave's start (100 MHz counter).", ""]
+    xcds = sorted({x["xcd"] for _, s in runs for x in s["xcd"]})
     lines.append("| launch | HIP events µs | span of the records µs | " +
-                 " | ".join(f"XCD {x['xcd']} loop end / last end" for x in runs[0][1]["xcd"]) + " |")
-    lines.append("|---" * (3 + len(runs[0][1]["xcd"])) + "|")
+                 " | ".join(f"XCD {x} loop end / last end" for x in xcds) + " |")
+    lines.append("|---" * (3 + len(xcds)) + "|")
     for i, (ev_us, s) in enumerate(runs):
-        cells = " | ".join(f"{x['loop_end_median']:.2f} / {x['last_end']:.2f}" for x in s["xcd"])
+        by = {x["xcd"]: x for x in s["xcd"]}
+        cells = " | ".join(f"{by[x]['loop_end_median']:.2f} / {by[x]['last_end']:.2f}" if x in by else "–"
+                           for x in xcds)
         lines.append(f"| {i} | {ev_us:.2f} | {s['span']:.2f} | {cells} |")
     last = runs[-1][1]
     lines += ["", f"Events of launch {len(runs) - 1} ({last['waves']} waves):", "",
