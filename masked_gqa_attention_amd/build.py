@@ -7,8 +7,9 @@ disabled and matrix-core accumulators in architectural registers, and
 linked into masked_gqa_attention_amd/libmgqa.so next to this file.  The
 same sources with the kernels compiled under MGQA_TIMELINE give
 libmgqa_timeline.so, the measurement build with per-wave timestamps
-(include/mgqa_timeline.h).  The build always recompiles (it is the "does it
-build" check).
+(include/mgqa_timeline.h), and mgqa_probe.hip gives libmgqa_probe.so, the
+throughput probes (include/mgqa_probe.h).  The build always recompiles (it
+is the "does it build" check).
 """
 from __future__ import annotations
 
@@ -25,10 +26,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmgqa.so")
 OUT_TIMELINE = os.path.join(PKG, "libmgqa_timeline.so")
+OUT_PROBE = os.path.join(PKG, "libmgqa_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["mgqa_api.cpp", "mgqa_kernels.hip", "mgqa_cache.hip"]
 TIMELINE_SOURCE = "mgqa_kernels.hip"  # the only source with timeline marks
+PROBE_SOURCE = "mgqa_probe.hip"
 
 ARCH = "gfx950"
 COMMON = [
@@ -79,15 +82,17 @@ def _link(objs, out: str, verbose: bool) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Builds libmgqa.so and libmgqa_timeline.so; returns the former's path."""
+    """Builds libmgqa.so, libmgqa_timeline.so and libmgqa_probe.so; returns
+    the first one's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = [(s, False) for s in SOURCES] + [(TIMELINE_SOURCE, True)]
+    jobs = [(s, False) for s in SOURCES] + [(TIMELINE_SOURCE, True), (PROBE_SOURCE, False)]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
     plain = objs[:len(SOURCES)]
-    timeline = [objs[-1] if s == TIMELINE_SOURCE else o for s, o in zip(SOURCES, plain)]
+    timeline = [objs[len(SOURCES)] if s == TIMELINE_SOURCE else o for s, o in zip(SOURCES, plain)]
     _link(plain, OUT, verbose)
     _link(timeline, OUT_TIMELINE, verbose)
+    _link([objs[-1]], OUT_PROBE, verbose)
     return OUT
 
 
