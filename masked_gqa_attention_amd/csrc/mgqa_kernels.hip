@@ -319,7 +319,19 @@ __device__ __forceinline__ void store_row(uint16_t* orow, const f32x4 (&o)[DV], 
 // row steps of a tile, is never inside a descriptor's range.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int KEYS, int CH, int PITCH, int NT>
+// Cache policy of a buffer load: 0, or kStreamLoad, the non-temporal bit
+// (the lines are kept in the caches only briefly).  The split-KV kernel
+// reads K/V with it when every (unit, split) key range is read by one
+// workgroup, or by the two column halves of a range at the same time: one
+// position block per unit, as in decode.  Measured against plain loads, same
+// box, median of 30 rounds: decode 4:1 over 8192 keys 47.0 -> 44.1 us, the
+// long windowed decode 13.4 -> 12.75 us, 4:1 over 2048 keys 16.6 -> 15.1 us.
+// With several position blocks re-reading a unit's rows through L2 it costs
+// those hits (300 queries over 4096 keys, 16 heads: 70 -> 103 us), so those
+// plans keep plain loads.
+constexpr int kStreamLoad = 2;
+
+template <int KEYS, int CH, int PITCH, int NT, int AUX = 0>
 struct RowTile {
   static constexpr int TOTAL = KEYS * CH;
   static constexpr int PER = (TOTAL + NT - 1) / NT;
@@ -348,7 +360,7 @@ struct RowTile {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
       const uint32_t vo = COMPACT ? voff[0] + (uint32_t)it * vstep : voff[it];
-      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0));
+      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, AUX));
     }
   }
   // Ring-buffer cache: logical key j of the unit lives in slot
@@ -365,7 +377,7 @@ struct RowTile {
       slot -= (slot >= S) ? S : 0;
       const bool ok = (TOTAL % NT == 0 || c < TOTAL) && (logical < Lkv) && (col0 + ch * 8 < d);
       const uint32_t vo = ok ? (uint32_t)(slot * d + col0 + ch * 8) * 2u : kOutOfRange;
-      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, 0));
+      r[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vo, 0, AUX));
     }
   }
   // Fused cache append: the chunks of keys app_pos .. app_pos+app_len-1 of the
@@ -1255,7 +1267,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe4_kernel(KernelArgs a) {
 // new rows as float32 inputs: the tiles holding them take them from there,
 // and one workgroup per new key writes it to its cache slot.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING, int NCOL>
+template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING, int NCOL, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KEYS = 32 * NW;
@@ -1324,8 +1336,8 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   // Staging registers for the next tile; with column halves (half-width V
   // tiles) a second set keeps two tiles in flight.
   constexpr bool TWO_AHEAD = NCOL == 2;
-  using KTile = RowTile<KEYS, DQK * 4, KP, NT>;
-  using VTile = RowTile<KEYS, DV * 2, VP, NT>;
+  using KTile = RowTile<KEYS, DQK * 4, KP, NT, STREAM ? kStreamLoad : 0>;
+  using VTile = RowTile<KEYS, DV * 2, VP, NT, STREAM ? kStreamLoad : 0>;
   KTile kt, kt2;
   VTile vt, vt2;
   kt.init(d, tid);
@@ -1985,13 +1997,18 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the instantiated shapes.
 // ---------------------------------------------------------------------------
+// Streaming (non-temporal) K/V loads when each unit has one position block
+// (no workgroup re-reads another's rows; see kStreamLoad).
 template <typename T, int DQK, int DV, int NQB, bool SOFTCAP, int NCOL = 1, int NW = kSplitWaves>
 static void launch_split(const dim3& grid, const KernelArgs& args, hipStream_t st) {
   const dim3 block(64 * NW);
-  if (NQB == 1 && args.ring_start >= 0)
-    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, NW, SOFTCAP, true, NCOL>), grid, block, 0, st, args);
+  if (NQB == 1 && args.ring_start >= 0)  // ring caches: decode only, one position block
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, 1, NW, SOFTCAP, true, NCOL, true>), grid, block, 0, st, args);
+  else if (args.n_pos_blk == 1)
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, NW, SOFTCAP, false, NCOL, true>), grid, block, 0, st, args);
   else
-    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, NW, SOFTCAP, false, NCOL>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((splitkv_kernel<T, DQK, DV, NQB, NW, SOFTCAP, false, NCOL, false>), grid, block, 0, st,
+                       args);
 }
 
 template <typename T, int DQK, int DV, bool SOFTCAP>
