@@ -33,7 +33,10 @@
  * with 16-byte loads, grid-stride over workgroups of 256 threads, and writes
  * the XOR of each thread's 32-bit words to sink[thread] (workgroups * 256
  * words): the XOR of all sink words equals the XOR of all words of src.
- * Errors as above (bytes not a multiple of 16: MGQA_ERR_SHAPE).
+ * nontemporal = 1 sets the non-temporal bit of every load (the lines stay in
+ * the caches only briefly), 0 reads with the default policy.  Errors as
+ * above (bytes not a multiple of 16, nontemporal not 0 or 1:
+ * MGQA_ERR_SHAPE).
  */
 #ifndef MGQA_PROBE_H
 #define MGQA_PROBE_H
@@ -56,7 +59,7 @@ extern "C" {
 
 int probe_alu(int kind, int workgroups, int waves, int iters, unsigned* sink, void* stream);
 
-int probe_read(const void* src, size_t bytes, int workgroups, unsigned* sink, void* stream);
+int probe_read(const void* src, size_t bytes, int workgroups, int nontemporal, unsigned* sink, void* stream);
 
 #ifdef __cplusplus
 }

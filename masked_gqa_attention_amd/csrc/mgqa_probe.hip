@@ -115,18 +115,29 @@ __global__ __launch_bounds__(1024) void probe_alu_kernel(int iters, unsigned* si
   sink[(size_t)blockIdx.x * blockDim.x + tid] = __builtin_bit_cast(uint32_t, s);
 }
 
+// A 16-byte load, plain or non-temporal (the nt bit: kept in the caches
+// only briefly).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, size_t n, unsigned* sink) {
   const size_t stride = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = x0, x2 = x0, x3 = x0;
   // Four independent loads in flight per thread.
   for (; i + 3 * stride < n; i += 4 * stride) {
-    x0 ^= src[i];
-    x1 ^= src[i + stride];
-    x2 ^= src[i + 2 * stride];
-    x3 ^= src[i + 3 * stride];
+    x0 ^= load16<NT>(src + i);
+    x1 ^= load16<NT>(src + i + stride);
+    x2 ^= load16<NT>(src + i + 2 * stride);
+    x3 ^= load16<NT>(src + i + 3 * stride);
   }
-  for (; i < n; i += stride) x0 ^= src[i];
+  for (; i < n; i += stride) x0 ^= load16<NT>(src + i);
   const u32x4 x = x0 ^ x1 ^ x2 ^ x3;
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
@@ -160,10 +171,15 @@ extern "C" int probe_alu(int kind, int workgroups, int waves, int iters, unsigne
   return e == hipSuccess ? MGQA_OK : MGQA_ERR_HIP;
 }
 
-extern "C" int probe_read(const void* src, size_t bytes, int workgroups, unsigned* sink, void* stream) {
+extern "C" int probe_read(const void* src, size_t bytes, int workgroups, int nontemporal, unsigned* sink,
+                          void* stream) {
   if (!src || !sink) return MGQA_ERR_NULL;
-  if (workgroups < 1 || bytes % 16 != 0) return MGQA_ERR_SHAPE;
-  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  if (workgroups < 1 || bytes % 16 != 0 || (nontemporal != 0 && nontemporal != 1)) return MGQA_ERR_SHAPE;
+  const dim3 grid((unsigned)workgroups), block(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    hipLaunchKernelGGL(probe_read_kernel<true>, grid, block, 0, st, static_cast<const u32x4*>(src), bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(probe_read_kernel<false>, grid, block, 0, st, static_cast<const u32x4*>(src), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? MGQA_OK : MGQA_ERR_HIP;
 }

@@ -12,7 +12,8 @@ Measures, each from HIP events around back-to-back launches on one stream:
   one, two and four workgroups of four waves per CU): matrix work alone,
   vector work alone, both;
 * the streaming read rate of device buffers of the 4:1 decode's size
-  (268.6 MB) and of 1 GiB, with three grid sizes.
+  (268.6 MB) and of 1 GiB, with plain and with non-temporal loads, with
+  three grid sizes.
 Prints a markdown report.  --quick: small sizes (a smoke check, not a
 measurement).
 """
@@ -55,7 +56,7 @@ def load() -> ctypes.CDLL:
         vp, i = ctypes.c_void_p, ctypes.c_int
         lib.probe_alu.argtypes = [i, i, i, i, vp, vp]
         lib.probe_alu.restype = i
-        lib.probe_read.argtypes = [vp, ctypes.c_size_t, i, vp, vp]
+        lib.probe_read.argtypes = [vp, ctypes.c_size_t, i, i, vp, vp]
         lib.probe_read.restype = i
         _lib = lib
     return _lib
@@ -102,19 +103,20 @@ def run_alu(kind: int, workgroups: int, waves: int, iters: int, reps: int = 5) -
     return out
 
 
-def run_read(nbytes: int, workgroups: int, reps: int = 5) -> dict:
+def run_read(nbytes: int, workgroups: int, nontemporal: bool = False, reps: int = 5) -> dict:
     lib = load()
     buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
     sink = torch.empty(workgroups * 256, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
     def launch():
-        rc = lib.probe_read(buf.data_ptr(), nbytes, workgroups, sink.data_ptr(), stream)
+        rc = lib.probe_read(buf.data_ptr(), nbytes, workgroups, int(nontemporal), sink.data_ptr(), stream)
         if rc != 0:
             raise RuntimeError(f"probe_read failed: {rc}")
 
     ms = _timed(launch, reps)
-    return {"bytes": nbytes, "workgroups": workgroups, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9}
+    return {"bytes": nbytes, "workgroups": workgroups, "nontemporal": nontemporal, "ms": ms,
+            "gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
 NAMES = {PROBE_MFMA: "bf16 16x16x32 products", PROBE_EXP: "v_exp_f32", PROBE_RCP: "v_rcp_f32",
@@ -140,8 +142,9 @@ def measure(quick: bool = False) -> dict:
             res["step"].append(r)
     res["read"] = []
     for nbytes in ((1 << 24,) if quick else (268566528, 1 << 30)):
-        for wgs in (CUS * 4, CUS * 8, CUS * 16):
-            res["read"].append(run_read(nbytes, wgs))
+        for nt in (False, True):
+            for wgs in (CUS * 4, CUS * 8, CUS * 16):
+                res["read"].append(run_read(nbytes, wgs, nt))
     return res
 
 
@@ -175,9 +178,10 @@ def markdown(res: dict, command: str) -> str:
         lines.append(f"| {NAMES[r['kind']]} | {r['per_cu']} | {r['ms']:.3f} | {r['iters']} | {per_step:.0f} "
                      f"| {per_step / r['per_cu']:.0f} |")
     lines += ["", "## Streaming read (16-byte loads, workgroups of 256 threads)", "",
-              "| bytes | workgroups | µs | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+              "| bytes | loads | workgroups | µs | GB/s | % of 8 TB/s |", "|---|---|---|---|---|---|"]
     for rd in res["read"]:
-        lines.append(f"| {rd['bytes']} | {rd['workgroups']} | {rd['ms'] * 1e3:.1f} | {rd['gbs']:.0f} "
+        kind = "non-temporal" if rd["nontemporal"] else "plain"
+        lines.append(f"| {rd['bytes']} | {kind} | {rd['workgroups']} | {rd['ms'] * 1e3:.1f} | {rd['gbs']:.0f} "
                      f"| {rd['gbs'] / 8000 * 100:.1f} |")
     lines.append("")
     return "\n".join(lines)

@@ -10,15 +10,16 @@ from masked_gqa_attention_amd import probe
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("nontemporal", [0, 1])
 @pytest.mark.parametrize("nbytes,workgroups", [(16, 1), (4096, 1), (1 << 20, 7), ((1 << 20) + 48, 256),
                                                (3 * (1 << 16) + 16, 1000)])
-def test_probe_read_xor(nbytes, workgroups):
-    print(f"probe_read bytes={nbytes} workgroups={workgroups}", flush=True)
+def test_probe_read_xor(nbytes, workgroups, nontemporal):
+    print(f"probe_read bytes={nbytes} workgroups={workgroups} nontemporal={nontemporal}", flush=True)
     g = torch.Generator().manual_seed(nbytes)
     host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
     buf = host.cuda()
     sink = torch.zeros(workgroups * 256, dtype=torch.int32, device="cuda")
-    rc = probe.load().probe_read(buf.data_ptr(), nbytes, workgroups, sink.data_ptr(),
+    rc = probe.load().probe_read(buf.data_ptr(), nbytes, workgroups, nontemporal, sink.data_ptr(),
                                  torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     torch.cuda.synchronize()

@@ -42,7 +42,8 @@ def test_probe_arguments_validated_before_hip():
     assert lib.probe_alu(probe.PROBE_MFMA, 1, 1, 0, sink, None) == _lib.MGQA_ERR_SHAPE
     assert lib.probe_alu(9, 1, 1, 1, sink, None) == _lib.MGQA_ERR_SHAPE
     assert lib.probe_alu(-1, 1, 1, 1, sink, None) == _lib.MGQA_ERR_SHAPE
-    assert lib.probe_read(None, 16, 1, sink, None) == _lib.MGQA_ERR_NULL
-    assert lib.probe_read(sink, 16, 1, None, None) == _lib.MGQA_ERR_NULL
-    assert lib.probe_read(sink, 24, 1, sink, None) == _lib.MGQA_ERR_SHAPE
-    assert lib.probe_read(sink, 16, 0, sink, None) == _lib.MGQA_ERR_SHAPE
+    assert lib.probe_read(None, 16, 1, 0, sink, None) == _lib.MGQA_ERR_NULL
+    assert lib.probe_read(sink, 16, 1, 0, None, None) == _lib.MGQA_ERR_NULL
+    assert lib.probe_read(sink, 24, 1, 0, sink, None) == _lib.MGQA_ERR_SHAPE
+    assert lib.probe_read(sink, 16, 0, 0, sink, None) == _lib.MGQA_ERR_SHAPE
+    assert lib.probe_read(sink, 16, 1, 2, sink, None) == _lib.MGQA_ERR_SHAPE
