@@ -1668,7 +1668,7 @@ __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
 // the V rows they multiply are other keys' rows, or zeros past Lkv).  Row sums come from the matrix cores (all-ones A
 // operand, the same 16-bit P as P.V).  The eight wave states then merge in
 // LDS in wave order; once a wave's P.V products are done, its region holds
-// its unnormalised rows (48 rows x DV*16 floats, exactly the region's bytes).
+// its unnormalised rows (48 rows of DV*16 floats, padded by 4).
 //
 // Q.K^T contracts the head size in DQK 32-deep matrix-core steps (head size
 // 72 padded to 96 with zeros).  A 16-deep product chained onto 32-deep ones
@@ -1682,11 +1682,16 @@ __global__ __launch_bounds__(64 * kEncWaves) void encoder_kernel(KernelArgs a) {
   constexpr int VPITCH = DV * 16;           // elements of one staged V row
   constexpr int CPR = DV * 2;               // 16-byte chunks of one staged V row
   constexpr int VLOADS = 32 * CPR / 64;     // 64-lane direct-to-LDS loads per step
-  constexpr int REGION = NS * 32 * VPITCH;  // elements of one wave's V region
-  constexpr int OPITCH = DV * 16;           // floats of one output row in the merge
+  // Floats of one output row in the merge: 16 bytes of padding put the 16
+  // rows of one 16-lane group of a row-block store on distinct LDS banks
+  // (unpadded, rows 4 apart shared banks: 4-way conflicts on every store).
+  constexpr int OPITCH = DV * 16 + 4;
+  constexpr int VELEMS = NS * 32 * VPITCH;    // elements of one wave's staged V rows
+  constexpr int OELEMS = NQB * 16 * OPITCH * 2;  // the same region holding its output rows
+  constexpr int REGION = VELEMS > OELEMS ? VELEMS : OELEMS;  // elements of one wave's region
   static_assert(DQK >= 1, "at least one 32-deep step");
   static_assert((32 * CPR) % 64 == 0, "a step's V rows are whole 64-lane loads");
-  static_assert(NQB * 16 * OPITCH * 4 == REGION * 2, "a wave's output rows fill its V region exactly");
+  static_assert(REGION % 8 == 0, "wave regions stay 16-byte aligned");
   __shared__ __attribute__((aligned(16))) uint16_t sv[NW * REGION];
   __shared__ float wm[NW][NQB * 16], wl[NW][NQB * 16];
   __shared__ float wf[NW][NQB * 16];  // merge weight of each wave's rows
