@@ -466,13 +466,17 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+constexpr int kKPad = 16;  // elements of padding after each staged K row
+
 // Per-wave tile work of the register-staged kernels (prefill_kernel,
 // splitkv_kernel).  A step is 32 keys: S^T blocks hh = 0, 1 of 16 keys each,
 // natural key order (block row rho is key kbase + 16*hh + rho), so lane group
 // g4 holds keys 4*g4 + i (hh = 0) and 16 + 4*g4 + i (hh = 1): the P^T operand
 // that the transposed V reads above produce.  K and V rows are padded to KP /
 // VP elements in LDS, which puts the rows of one fragment read on distinct
-// banks.
+// banks.  K rows take 32 bytes of padding (kKPad): with 16, the K fragment
+// reads of the split-KV kernel still conflicted (SQ_LDS_BANK_CONFLICT
+// 524288 per launch of the 4:1 decode, 0 with 32; 44.1 -> 43.8 us).
 
 // One 32-key step: scores, softcap, mask, online softmax and P.V; each
 // fragment is read from LDS right before its products.  The MASK instance
@@ -617,8 +621,8 @@ template <typename T, int DQK, int DV, int NQB, int NWAVES, bool SOFTCAP>
 __global__ __launch_bounds__(NWAVES * 64) void prefill_kernel(KernelArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int KEYS = kPrefillKeys;
-  constexpr int KP = DQK * 32 + 8;   // 16 rows of a K read land on distinct banks
-  constexpr int VP = DV * 16 + 16;   // 4 rows x 32 B of a transposed V read do too
+  constexpr int KP = DQK * 32 + kKPad;  // 16 rows of a K read land on distinct banks
+  constexpr int VP = DV * 16 + 16;      // 4 rows x 32 B of a transposed V read do too
   constexpr int STAGE = KEYS * (KP + VP);
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -1271,7 +1275,7 @@ template <typename T, int DQK, int DV, int NQB, int NW, bool SOFTCAP, bool RING,
 __global__ __launch_bounds__(NW * 64) void splitkv_kernel(KernelArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KEYS = 32 * NW;
-  constexpr int KP = DQK * 32 + 8;
+  constexpr int KP = DQK * 32 + kKPad;
   constexpr int VP = DV * 16 + 16;
   constexpr int DVP = DV * 16;
   constexpr int OP = DVP + 4;  // LDS pitch of the merged wave outputs (floats)
